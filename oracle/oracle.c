@@ -1,0 +1,229 @@
+/*
+ * oracle.c -- the CPU oracle for the block-wise INT8 W8A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Plain scalar C, written from the
+ * pages' description of the method and nothing else.  It shares no code,
+ * header, table or helper with the HIP library, and only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg may call it.
+ *
+ * Pages cited (by title and section):
+ *   [BW8] "[SGLang] Block-wise INT8: 블록 단위 정수 양자화"
+ *         (blog.secrett2633.cloud, opensource/sglang/blockwise-int8)
+ *   [SQ]  "양자화 (Quantization)" -- the SGLang quantization page of the
+ *         data-sketchers wiki (platform matrix and W8A8 notes)
+ *
+ * Precision.  Quantisation decides integers, so it runs in IEEE binary32 as
+ * the stored fp32 scales dictate ([BW8], design rationale item 3: scales are
+ * fp32).  The GEMM's block sums are exact integers; their rescaled sum is
+ * taken in binary64 and rounded once to bf16, so the oracle gives the exact
+ * value (to ~1e-15) that the fp32 kernels approximate.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (no FTZ/DAZ, default round-to-nearest-even mode).
+ *
+ * Return codes: 0 = ok, -1 = bad argument, -2 = non-finite input.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* bf16 <-> binary32/binary64                                           */
+/* ------------------------------------------------------------------ */
+
+/* A bf16 value is the upper half of a binary32 with the same bits, so the
+ * widening is exact. */
+static float bf16_bits_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary64 value to the nearest bf16 (8 significant bits, exponent
+ * range of binary32), ties to even, in ONE rounding step.  Written from the
+ * IEEE-754 definition: find the quantum (weight of the last kept bit) of the
+ * binade that holds |v|, scale by it, round to an integer with the default
+ * ties-to-even mode, scale back. */
+uint16_t oracle_f64_to_bf16(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    int e;
+    frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    int q = (e - 1) - 7;          /* quantum of an 8-bit significand */
+    if (q < -133) q = -133;       /* bf16 subnormal quantum is 2^-133 */
+    double r = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (r >= 0x1p128) return (uint16_t)(sign | 0x7F80u); /* overflow -> inf */
+    float f = (float)r;           /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* Exposed for the pin tests. */
+float oracle_bf16_to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
+
+/* ------------------------------------------------------------------ */
+/* Scale-tensor shape                                                   */
+/* ------------------------------------------------------------------ */
+
+/* [BW8] §2 (weight and block-scale creation): the fp32 scale tensor of an
+ * int8 weight [N, K] has one entry per (block_n x block_k) block, rounding
+ * partial blocks up: [ceil(N/block_n), ceil(K/block_k)]. */
+int oracle_scale_shape(int64_t N, int64_t K, int64_t block_n, int64_t block_k,
+                       int64_t *rows, int64_t *cols)
+{
+    if (N < 0 || K < 0 || block_n <= 0 || block_k <= 0 || !rows || !cols) return -1;
+    *rows = (N + block_n - 1) / block_n;
+    *cols = (K + block_k - 1) / block_k;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O1: dynamic activation quantisation                                  */
+/* ------------------------------------------------------------------ */
+
+/* [BW8] §4 (inference apply): with no static input scale the activation
+ * scale is computed at run time, per token; [BW8] structure diagram and §1:
+ * only the dynamic scheme exists; design rationale item 3: int8 range with
+ * fp32 scales.  Reading taken: one scale per (token m, group g of block_k
+ * consecutive K entries), the last group holding the K % block_k remainder.
+ *
+ *   amax   = max |x[m,k]| over the group                (exact)
+ *   s      = amax / 127                                 (binary32, RN)
+ *   q[m,k] = 0 if s == 0, else clamp(rne(x[m,k] / s), -127, 127)
+ *
+ * x is bf16 bits [M, ldx] (row stride ldx >= K); xq is int8 [M, K];
+ * xs is fp32 [M, ceil(K/block_k)]. */
+int oracle_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                     int64_t block_k, int8_t *xq, float *xs)
+{
+    if (M < 0 || K < 0 || ldx < K || block_k <= 0) return -1;
+    if ((M > 0 && K > 0) && (!x || !xq || !xs)) return -1;
+    const int64_t KB = (K + block_k - 1) / block_k;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = x + m * ldx;
+        for (int64_t g = 0; g < KB; ++g) {
+            const int64_t k0 = g * block_k;
+            const int64_t k1 = (k0 + block_k < K) ? k0 + block_k : K;
+            float amax = 0.0f;
+            for (int64_t k = k0; k < k1; ++k) {
+                float v = bf16_bits_to_f32(row[k]);
+                if (!isfinite(v)) return -2;
+                float a = fabsf(v);
+                if (a > amax) amax = a;
+            }
+            const float s = amax / 127.0f;
+            xs[m * KB + g] = s;
+            for (int64_t k = k0; k < k1; ++k) {
+                float q = 0.0f;
+                if (s != 0.0f) {
+                    q = rintf(bf16_bits_to_f32(row[k]) / s);
+                    if (q > 127.0f) q = 127.0f;
+                    if (q < -127.0f) q = -127.0f;
+                }
+                xq[m * K + k] = (int8_t)q;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O2: block-scaled int8 GEMM                                           */
+/* ------------------------------------------------------------------ */
+
+/* [BW8] structure diagram and §2: weight int8 [N, K] (output dim 0, input
+ * dim 1), scale fp32 [ceil(N/block_n), ceil(K/block_k)]; §4: the linear
+ * takes the int8 weight, its block scales, the dynamic activation scales and
+ * an optional bias; design rationale item 3: dequantisation multiplies by
+ * the fp32 scales.  Reading taken (y = x . W^T):
+ *
+ *   y[m,n] = sum_g ( sum_{k in g} xq[m,k] * w[n,k] ) * xs[m,g] * ws[n/bn, g]
+ *            (+ bias[n]),  rounded once to bf16
+ *
+ * The inner sums are exact integers; the outer sum runs in binary64 over
+ * ascending g.  The result is written as binary64 (y64, may be NULL) and/or
+ * bf16 bits (y16, may be NULL). */
+static int gemm_core(const int8_t *xq, const float *xs, const int8_t *w,
+                     const float *ws, const uint16_t *bias, double *y64,
+                     uint16_t *y16, int64_t M, int64_t N, int64_t K,
+                     int64_t block_n, int64_t block_k)
+{
+    if (M < 0 || N < 0 || K < 0 || block_n <= 0 || block_k <= 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (!xq || !xs || !w || !ws || (!y64 && !y16)) return -1;
+    const int64_t KB = (K + block_k - 1) / block_k;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t nb = n / block_n;
+            double acc_y = 0.0;
+            for (int64_t g = 0; g < KB; ++g) {
+                const int64_t k0 = g * block_k;
+                const int64_t k1 = (k0 + block_k < K) ? k0 + block_k : K;
+                int64_t acc = 0;
+                for (int64_t k = k0; k < k1; ++k)
+                    acc += (int64_t)xq[m * K + k] * (int64_t)w[n * K + k];
+                const double t = (double)xs[m * KB + g] * (double)ws[nb * KB + g];
+                acc_y += (double)acc * t;
+            }
+            if (bias) acc_y += (double)bf16_bits_to_f32(bias[n]);
+            if (y64) y64[m * N + n] = acc_y;
+            if (y16) y16[m * N + n] = oracle_f64_to_bf16(acc_y);
+        }
+    }
+    return 0;
+}
+
+int oracle_gemm(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                int64_t block_n, int64_t block_k)
+{
+    if (!y && M > 0 && N > 0) return -1;
+    return gemm_core(xq, xs, w, ws, bias, NULL, y, M, N, K, block_n, block_k);
+}
+
+int oracle_gemm_f64(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                    const uint16_t *bias, double *y, int64_t M, int64_t N, int64_t K,
+                    int64_t block_n, int64_t block_k)
+{
+    if (!y && M > 0 && N > 0) return -1;
+    return gemm_core(xq, xs, w, ws, bias, y, NULL, M, N, K, block_n, block_k);
+}
+
+/* ------------------------------------------------------------------ */
+/* O2 per expert: the grouped (FusedMoE) form                           */
+/* ------------------------------------------------------------------ */
+
+/* [BW8] §5 (MoE weights): every expert e owns an int8 weight and its own
+ * fp32 block scales, stacked on a leading expert axis: w [E, N, K],
+ * ws [E, ceil(N/bn), ceil(K/bk)]; §6: the MoE runner applies the same
+ * int8 W8A8 block arithmetic per expert.  Rows arrive sorted by expert:
+ * rows [off[e], off[e+1]) use expert e.  Each segment is O2 with that
+ * expert's weight and scales.  off is a host array of E+1 entries with
+ * off[0] = 0, off[E] = R, non-decreasing. */
+int oracle_moe_gemm(const int8_t *xq, const float *xs, const int32_t *off,
+                    const int8_t *w, const float *ws, uint16_t *y,
+                    int64_t R, int64_t N, int64_t K, int64_t E,
+                    int64_t block_n, int64_t block_k)
+{
+    if (R < 0 || N < 0 || K < 0 || E <= 0 || block_n <= 0 || block_k <= 0 || !off) return -1;
+    if (off[0] != 0 || off[E] != R) return -1;
+    for (int64_t e = 0; e < E; ++e)
+        if (off[e + 1] < off[e]) return -1;
+    const int64_t NB = (N + block_n - 1) / block_n;
+    const int64_t KB = (K + block_k - 1) / block_k;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t r0 = off[e], rows = off[e + 1] - off[e];
+        if (rows == 0) continue;
+        int rc = oracle_gemm(xq + r0 * K, xs + r0 * KB, w + e * N * K, ws + e * NB * KB,
+                             NULL, y + r0 * N, rows, N, K, block_n, block_k);
+        if (rc) return rc;
+    }
+    return 0;
+}
