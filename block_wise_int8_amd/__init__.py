@@ -1,0 +1,198 @@
+"""Block-wise INT8 W8A8 linear for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libblockint8.so`` (declared in
+``include/blockint8.h``).  It only marshals arguments: every step of the
+computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and streams.  There is no CPU fallback: if the library is missing or a
+tensor is not on a HIP device, the call raises.
+
+Entry points (same names as the C ABI, without the ``blockint8_`` prefix):
+
+* :func:`quant_act`  -- bf16 [M, K] -> int8 [M, K] + fp32 [M, ceil(K/128)]
+* :func:`gemm`       -- y = bf16(block-scaled int8 GEMM (+ bias)), [M, N]
+* :func:`moe_gemm`   -- the same per expert over expert-sorted rows
+* :func:`linear`     -- quant_act followed by gemm (the dynamic-scale linear)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "moe_gemm",
+           "linear", "BLOCK"]
+
+BLOCK = 128
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libblockint8.so"
+_lib = None
+
+BI8_OK = 0
+_STATUS_NAMES = {0: "BI8_OK", 1: "BI8_ERR_NULL", 2: "BI8_ERR_SHAPE", 3: "BI8_ERR_BLOCK",
+                 4: "BI8_ERR_ALIGN", 5: "BI8_ERR_HIP"}
+
+
+class BlockInt8Error(RuntimeError):
+    """A C ABI call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load() -> ctypes.CDLL:
+    """Load ``libblockint8.so`` (building it first if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.blockint8_status_string.argtypes = [i32]
+    lib.blockint8_status_string.restype = ctypes.c_char_p
+    lib.blockint8_last_error.argtypes = []
+    lib.blockint8_last_error.restype = ctypes.c_char_p
+    lib.blockint8_quant_act.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp]
+    lib.blockint8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.blockint8_moe_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm"):
+        getattr(lib, f).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != BI8_OK:
+        msg = load().blockint8_last_error().decode(errors="replace")
+        raise BlockInt8Error(status, msg)
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a HIP device (got %s); there is no CPU path" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims (got shape %s)" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def scale_shape(N: int, K: int, block_n: int = BLOCK, block_k: int = BLOCK):
+    """Shape of a block-scale tensor for an int8 [N, K] weight: ceil both dims."""
+    return (N + block_n - 1) // block_n, (K + block_k - 1) // block_k
+
+
+def quant_act(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tensor | None = None,
+              block_k: int = BLOCK):
+    """Dynamic per-(token, 128-group) quantisation of bf16 ``x`` [M, K].
+
+    Returns ``(xq int8 [M, K], xs float32 [M, ceil(K/128)])``.  ``x`` may have
+    a row stride (leading dimension) larger than K.
+    """
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a 2-D bfloat16 tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device; there is no CPU path")
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    M, K = x.shape
+    KB = (K + block_k - 1) // block_k
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M, KB), dtype=torch.float32, device=x.device)
+    _need(xq, "xq", torch.int8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    if tuple(xq.shape) != (M, K) or tuple(xs.shape) != (M, KB):
+        raise ValueError("output shapes must be [M, K] and [M, ceil(K/128)]")
+    ldx = x.stride(0) if M > 1 else K
+    _check(load().blockint8_quant_act(_ptr(x), M, K, ldx, block_k, _ptr(xq), _ptr(xs),
+                                      _stream_handle(x.device)))
+    return xq, xs
+
+
+def gemm(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tensor,
+         bias: torch.Tensor | None = None, y: torch.Tensor | None = None,
+         block=(BLOCK, BLOCK)) -> torch.Tensor:
+    """Block-scaled int8 GEMM ``y = x . W^T`` -> bf16 [M, N]."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    _need(w, "w", torch.int8, 2)
+    _need(ws, "ws", torch.float32, 2)
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] with K = %d (got %s)" % (K, tuple(w.shape)))
+    NB, KB = scale_shape(N, K, *block)
+    if tuple(xs.shape) != (M, KB) or tuple(ws.shape) != (NB, KB):
+        raise ValueError("scale shapes must be xs [M, %d] and ws [%d, %d]" % (KB, NB, KB))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must be [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    _check(load().blockint8_gemm(_ptr(xq), _ptr(xs), _ptr(w), _ptr(ws), _ptr(bias), _ptr(y),
+                                 M, N, K, block[0], block[1], _stream_handle(xq.device)))
+    return y
+
+
+def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w: torch.Tensor,
+             ws: torch.Tensor, y: torch.Tensor | None = None, block=(BLOCK, BLOCK)) -> torch.Tensor:
+    """Grouped block-scaled int8 GEMM over expert-sorted rows -> bf16 [R, N].
+
+    ``expert_offsets`` is int32 [E+1] on the device (rows [off[e], off[e+1])
+    use expert e); ``w`` is int8 [E, N, K], ``ws`` fp32 [E, ceil(N/128), ceil(K/128)].
+    """
+    _need(xq, "xq", torch.int8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _need(w, "w", torch.int8, 3)
+    _need(ws, "ws", torch.float32, 3)
+    R, K = xq.shape
+    E, N, Kw = w.shape
+    if Kw != K:
+        raise ValueError("w must be [E, N, K] with K = %d" % K)
+    if expert_offsets.shape[0] != E + 1:
+        raise ValueError("expert_offsets must have E + 1 = %d entries" % (E + 1))
+    NB, KB = scale_shape(N, K, *block)
+    if tuple(xs.shape) != (R, KB) or tuple(ws.shape) != (E, NB, KB):
+        raise ValueError("scale shapes must be xs [R, %d] and ws [E, %d, %d]" % (KB, NB, KB))
+    if y is None:
+        y = torch.empty((R, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (R, N):
+        raise ValueError("y must be [R, N]")
+    _check(load().blockint8_moe_gemm(_ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(w), _ptr(ws),
+                                     _ptr(y), R, N, K, E, block[0], block[1],
+                                     _stream_handle(xq.device)))
+    return y
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tensor | None = None,
+           block=(BLOCK, BLOCK)) -> torch.Tensor:
+    """Block-wise INT8 linear with dynamic activation scales: quant_act then gemm."""
+    xq, xs = quant_act(x, block_k=block[1])
+    return gemm(xq, xs, w, ws, bias=bias, block=block)

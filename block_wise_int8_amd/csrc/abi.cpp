@@ -1,0 +1,149 @@
+// C ABI of the block-wise INT8 library: argument checks on the host, then
+// one launch on the caller's stream.  See include/blockint8.h for the
+// contract of each entry point.
+//
+// The checks mirror the configuration rules of the page "[SGLang] Block-wise
+// INT8" (blog.secrett2633.cloud), section 1: weights arrive as int8 (the only
+// weight type accepted here), the block has two dimensions (block_n,
+// block_k), and only dynamic activation scales exist (there is no argument
+// for a static one).  Everything is checked before any HIP call, so a bad
+// call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/blockint8.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int32_t ok() {
+    g_last_error[0] = '\0';
+    return BI8_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxRows = 0x7FFFFFFFll;
+
+int32_t check_block(const char *fn, int32_t block_n, int32_t block_k) {
+    if (block_n <= 0 || block_k <= 0)
+        return fail(BI8_ERR_BLOCK, "%s: block size [%d, %d] must be two positive integers", fn,
+                    block_n, block_k);
+    if (block_n != 128 || block_k != 128)
+        return fail(BI8_ERR_BLOCK, "%s: only the [128, 128] block is implemented, got [%d, %d]",
+                    fn, block_n, block_k);
+    return BI8_OK;
+}
+
+int32_t check_k(const char *fn, int64_t K) {
+    if (K <= 0 || K > BI8_MAX_K)
+        return fail(BI8_ERR_SHAPE, "%s: K = %lld out of range [1, %d]", fn, (long long)K, BI8_MAX_K);
+    if (K % 16 != 0)
+        return fail(BI8_ERR_ALIGN, "%s: K = %lld must be a multiple of 16", fn, (long long)K);
+    return BI8_OK;
+}
+
+int32_t hip_status(const char *fn, hipError_t e) {
+    if (e != hipSuccess) return fail(BI8_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+// Checks shared by the dense and grouped GEMM.
+int32_t check_gemm_common(const char *fn, const int8_t *xq, const float *xs, const int8_t *w,
+                          const float *ws, const uint16_t *y, int64_t rows, int64_t N, int64_t K,
+                          int32_t block_n, int32_t block_k) {
+    if (rows < 0 || rows > kMaxRows)
+        return fail(BI8_ERR_SHAPE, "%s: row count %lld out of range", fn, (long long)rows);
+    if (N <= 0 || N > kMaxRows)
+        return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
+    int32_t s = check_k(fn, K);
+    if (s) return s;
+    if ((s = check_block(fn, block_n, block_k))) return s;
+    if (rows == 0) return BI8_OK;
+    if (!xq || !xs || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned(xq, 16) || !aligned(w, 16))
+        return fail(BI8_ERR_ALIGN, "%s: xq and w must be 16-byte aligned", fn);
+    if (!aligned(xs, 4) || !aligned(ws, 4))
+        return fail(BI8_ERR_ALIGN, "%s: xs and ws must be 4-byte aligned", fn);
+    if (!aligned(y, 2)) return fail(BI8_ERR_ALIGN, "%s: y must be 2-byte aligned", fn);
+    return BI8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *blockint8_status_string(int32_t status) {
+    switch (status) {
+        case BI8_OK: return "BI8_OK";
+        case BI8_ERR_NULL: return "BI8_ERR_NULL";
+        case BI8_ERR_SHAPE: return "BI8_ERR_SHAPE";
+        case BI8_ERR_BLOCK: return "BI8_ERR_BLOCK";
+        case BI8_ERR_ALIGN: return "BI8_ERR_ALIGN";
+        case BI8_ERR_HIP: return "BI8_ERR_HIP";
+        default: return "BI8_ERR_UNKNOWN";
+    }
+}
+
+const char *blockint8_last_error(void) { return g_last_error; }
+
+int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int32_t block_k,
+                            int8_t *xq, float *xs, void *stream) {
+    static const char fn[] = "blockint8_quant_act";
+    if (M < 0 || M > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: M = %lld out of range", fn, (long long)M);
+    int32_t s = check_k(fn, K);
+    if (s) return s;
+    if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
+    if ((s = check_block(fn, 128, block_k))) return s;
+    if (M == 0) return ok();
+    if (!x || !xq || !xs) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
+    if (!aligned(x, 16) || !aligned(xq, 16))
+        return fail(BI8_ERR_ALIGN, "%s: x and xq must be 16-byte aligned", fn);
+    if (!aligned(xs, 4)) return fail(BI8_ERR_ALIGN, "%s: xs must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_quant_act(x, M, K, ldx, xq, xs,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                       const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                       int32_t block_n, int32_t block_k, void *stream) {
+    static const char fn[] = "blockint8_gemm";
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, M, N, K, block_n, block_k);
+    if (s) return s;
+    if (M == 0) return ok();
+    if (bias && !aligned(bias, 2)) return fail(BI8_ERR_ALIGN, "%s: bias must be 2-byte aligned", fn);
+    const bi8::GemmPath path = bi8::select_gemm_path(M, N, K);
+    return hip_status(fn, bi8::launch_gemm(path, xq, xs, w, ws, bias, y, M, N, K,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
+                           const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
+                           int64_t K, int32_t E, int32_t block_n, int32_t block_k, void *stream) {
+    static const char fn[] = "blockint8_moe_gemm";
+    if (E <= 0 || E > 65536) return fail(BI8_ERR_SHAPE, "%s: E = %d out of range [1, 65536]", fn, E);
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, R, N, K, block_n, block_k);
+    if (s) return s;
+    if (R == 0) return ok();
+    if (!expert_offsets) return fail(BI8_ERR_NULL, "%s: NULL expert_offsets", fn);
+    if (!aligned(expert_offsets, 4))
+        return fail(BI8_ERR_ALIGN, "%s: expert_offsets must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_moe_gemm(xq, xs, expert_offsets, w, ws, y, R, N, K, E,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device-side helpers shared by the block-wise INT8 kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi8 {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define BI8_LDS __attribute__((address_space(3)))
+
+// The [128, 128] block this library implements.
+constexpr int kBlock = 128;
+
+// Offset that lies beyond every buffer's num_records: a buffer load with it
+// returns zero without touching memory.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (IEEE-754 roundTiesToEven on the
+// 16 dropped bits); NaN becomes the canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Raw buffer resource over [base, base + num_bytes): loads at offsets past the
+// end return zero (gfx9 raw-buffer range check, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t n) {
+    return n <= 0 ? 0u : (n >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)n);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that is also a compiler memory barrier but does not make
+// the compiler drain outstanding global loads first (the LDS fills issued by
+// buffer-to-LDS loads are waited for explicitly with wait_vmcnt).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_barrier" ::: "memory");
+}
+
+}  // namespace bi8

@@ -1,0 +1,515 @@
+// Block-scaled int8 GEMM kernels for gfx950: y = bf16( sum_g acc_g * xs * ws ).
+//
+// Page "[SGLang] Block-wise INT8" (blog.secrett2633.cloud): structure diagram
+// and section 2 (int8 weight [N, K], fp32 scale per 128 x 128 block, scale
+// tensor [ceil(N/128), ceil(K/128)]); section 4 (the linear consumes the int8
+// weight, its block scales and dynamic per-token activation scales, plus an
+// optional bias); section 5/6 (per-expert weights and scales for MoE);
+// design rationale item 1 (a 128 x 128 block matches the GEMM tile) and
+// item 3 (fp32 scales multiply on dequantisation).
+//
+// Both kernels put the WEIGHT rows in the MFMA's A operand (rows of the MFMA
+// result = output columns n) and the activation rows in the B operand
+// (columns of the result = tokens m).  A lane of the 32x32 (16x16) result then
+// holds a single token and 16 (4) output columns that all sit in one 128-row
+// weight block, so the per-block rescale needs ONE fp32 factor per lane:
+// t = xs[m, g] * ws[n / 128, g], applied as y = fma(float(acc_int32), t, y).
+//
+// Paths:
+//  * skinny (M <= 32, decode): HBM streaming of W.  A workgroup owns 16
+//    weight rows; its 8 waves split K.  Each lane loads 32 contiguous bytes of
+//    one weight row per 128-block straight into registers (no LDS), issues all
+//    of its loads before the first MFMA (v_mfma_i32_16x16x64_i8), and the
+//    waves' fp32 partials are summed through LDS.
+//  * tiled (M > 32, prefill, MoE): int8 MFMA v_mfma_i32_32x32x32_i8.  A
+//    workgroup computes a (64*WN) x (64*WM) tile (W rows x X rows), one 64x64
+//    sub-tile per wave.  K advances one 128-block per step; both operand tiles
+//    are staged in LDS by buffer->LDS loads (no VGPR round trip) through a
+//    3-deep ring, one LDS array per stage, rows of 128 B with the 16-byte
+//    chunks XOR-swizzled so the MFMA fragment reads are bank-conflict free.
+//    The per-block activation scales ride in the same stage.  Out-of-range
+//    rows (M, N tails, MoE segment ends) and the K tail read as zero through
+//    the buffer range check, which is exactly zero padding.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bi8 {
+
+namespace {
+
+struct GemmArgs {
+    const int8_t *xq;
+    const float *xs;
+    const int8_t *w;
+    const float *ws;
+    const uint16_t *bias;
+    uint16_t *y;
+    const int32_t *offsets;   // MoE only: [E + 1] row offsets per expert
+    int64_t M;                // rows (R for MoE)
+    int64_t N;
+    int64_t K;
+    int64_t KB;               // ceil(K / 128)
+    int64_t NB;               // ceil(N / 128)
+    int64_t tiles_m;          // dense: ceil(M / BM); MoE: upper bound of m-tiles
+    int64_t tiles_n;
+    int32_t E;
+    int32_t wide_store;       // y rows allow 8-byte stores (N % 4 == 0, y 8-byte aligned)
+};
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ i32x4 as_i32x4(u32x4 v) {
+    return __builtin_bit_cast(i32x4, v);
+}
+
+// ---------------------------------------------------------------------------
+// Skinny path (M <= 32)
+// ---------------------------------------------------------------------------
+
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyUnroll = 4;
+
+template <int MT>   // 16-token column tiles: 1 for M <= 16, 2 for M <= 32
+__global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs p,
+                                                                       int32_t blocks_per_wave) {
+    __shared__ float red[kSkinnyWaves][MT][64][4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = lane & 15;    // weight row in the tile, and token column
+    const int quad = lane >> 4;   // 32-byte quarter of a 128-wide K block
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t K = p.K, KB = p.KB;
+
+    // Each range covers only what this workgroup may read (<= 2^31 bytes since
+    // K <= 2^23), so kOobOffset always lies past it.
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(p.w + n0 * K, clamp_bytes((p.N - n0 < 16 ? p.N - n0 : 16) * K));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, clamp_bytes(p.M * K));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs, clamp_bytes(p.M * KB * 4));
+    const float *ws_row = p.ws + (n0 / kBlock) * KB;
+
+    const int64_t b_begin = (int64_t)wave * blocks_per_wave;
+    const int64_t b_end = b_begin + blocks_per_wave < KB ? b_begin + blocks_per_wave : KB;
+
+    f32x4 yv[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) yv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t b0 = b_begin; b0 < b_end; b0 += kSkinnyUnroll) {
+        i32x4 wa[kSkinnyUnroll][2];
+        i32x4 xb[kSkinnyUnroll][MT][2];
+        float xsv[kSkinnyUnroll][MT];
+        float wsv[kSkinnyUnroll];
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+            const int64_t b = b0 + u;
+            const bool ok = b < b_end;
+            const int64_t kk = b * kBlock + quad * 32;
+            const bool in0 = ok && kk < K, in1 = ok && kk + 16 < K;
+            wa[u][0] = as_i32x4(buf_load16(wr, in0 ? (uint32_t)(row * K + kk) : kOobOffset));
+            wa[u][1] = as_i32x4(buf_load16(wr, in1 ? (uint32_t)(row * K + kk + 16) : kOobOffset));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int64_t tok = mt * 16 + row;
+                xb[u][mt][0] = as_i32x4(buf_load16(xr, in0 ? (uint32_t)(tok * K + kk) : kOobOffset));
+                xb[u][mt][1] =
+                    as_i32x4(buf_load16(xr, in1 ? (uint32_t)(tok * K + kk + 16) : kOobOffset));
+                xsv[u][mt] = buf_load_f32(sr, ok ? (uint32_t)((tok * KB + b) * 4) : kOobOffset);
+            }
+            wsv[u] = ws_row[ok ? b : KB - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kSkinnyUnroll; ++u) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], xb[u][mt][0],
+                                                                  i32x4{0, 0, 0, 0}, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], xb[u][mt][1], acc, 0, 0, 0);
+                const float t = xsv[u][mt] * wsv[u];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) yv[mt][i] = fmaf((float)acc[i], t, yv[mt][i]);
+            }
+        }
+    }
+
+    // 16x16 result layout: lane -> token column (lane & 15), weight rows
+    // 4 * (lane >> 4) + i.  Sum the waves' partials through LDS.
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][mt][lane][i] = yv[mt][i];
+    __syncthreads();
+    for (int t = threadIdx.x; t < MT * 256; t += kSkinnyWaves * 64) {
+        const int mt = t >> 8, c = (t >> 4) & 15, r = t & 15;
+        const int src = c + 16 * (r >> 2), i = r & 3;
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < kSkinnyWaves; ++v) s += red[v][mt][src][i];
+        const int64_t tok = mt * 16 + c, n = n0 + r;
+        if (tok < p.M && n < p.N) {
+            if (p.bias) s += bf16_bits_to_f32(p.bias[n]);
+            p.y[tok * p.N + n] = (uint16_t)f32_to_bf16_bits(s);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled path
+// ---------------------------------------------------------------------------
+
+template <int WN, int WM>
+struct TileCfg {
+    static constexpr int kWaves = WN * WM;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kBN = 64 * WN;              // weight rows per tile
+    static constexpr int kBM = 64 * WM;              // activation rows per tile
+    static constexpr int kWOff = 0;                  // LDS layout of one stage
+    static constexpr int kXOff = kBN * 128;
+    static constexpr int kSOff = kXOff + kBM * 128;
+    static constexpr int kStageBytes = kSOff + kBM * 4;
+    static constexpr int kWLoads = 8 / WM;           // 1 KB W pieces per wave per stage
+    static constexpr int kXLoads = 8 / WN;           // 1 KB X pieces per wave per stage
+    static constexpr int kTileLoads = kWLoads + kXLoads;
+    static_assert(8 % WM == 0 && 8 % WN == 0, "load split");
+};
+
+// Spread consecutive workgroup ids (dispatched round-robin over the 8 XCDs)
+// so that each XCD receives a contiguous range of tiles and its L2 sees
+// neighbouring tiles.  Bijective on [0, total).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
+    const int64_t q = total >> 3, r = total & 7;
+    const int64_t xcd = bid & 7, slot = bid >> 3;
+    return xcd * q + (xcd < r ? xcd : r) + slot;
+}
+
+constexpr int64_t kGroupM = 8;   // m-tiles per group in the tile order
+
+struct Tile {
+    int64_t n0;    // first weight row / output column
+    int64_t m0;    // first activation row (global row of xq, xs, y)
+    int64_t rows;  // valid activation rows in this tile
+    const int8_t *w;
+    const float *ws;
+};
+
+template <int BN, int BM, bool MOE>
+__device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
+    const int64_t total = p.tiles_m * p.tiles_n;
+    const int64_t tid = xcd_remap(blockIdx.x, total);
+    // grouped order: kGroupM m-tiles advance together along n
+    const int64_t group = tid / (kGroupM * p.tiles_n);
+    const int64_t first_m = group * kGroupM;
+    const int64_t gsize = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
+    const int64_t in = tid - group * kGroupM * p.tiles_n;
+    int64_t tm = first_m + in % gsize;
+    const int64_t tn = in / gsize;
+    t.n0 = tn * BN;
+    if constexpr (!MOE) {
+        t.m0 = tm * BM;
+        t.rows = p.M - t.m0 < BM ? p.M - t.m0 : BM;
+        t.w = p.w;
+        t.ws = p.ws;
+        return true;
+    } else {
+        for (int32_t e = 0; e < p.E; ++e) {
+            // clamp to [0, R] so that offsets breaking the precondition can
+            // never address rows outside xq / y
+            int64_t a = p.offsets[e], b = p.offsets[e + 1];
+            a = a < 0 ? 0 : (a > p.M ? p.M : a);
+            b = b < a ? a : (b > p.M ? p.M : b);
+            const int64_t cnt = (b - a + BM - 1) / BM;
+            if (tm < cnt) {
+                t.m0 = a + tm * BM;
+                t.rows = b - t.m0 < BM ? b - t.m0 : BM;
+                t.w = p.w + (int64_t)e * p.N * p.K;
+                t.ws = p.ws + (int64_t)e * p.NB * p.KB;
+                return true;
+            }
+            tm -= cnt;
+        }
+        return false;
+    }
+}
+
+template <int WN, int WM, bool MOE>
+__global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
+    using C = TileCfg<WN, WM>;
+    __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds2[C::kStageBytes];
+
+    Tile t;
+    if (!decode_tile<C::kBN, C::kBM, MOE>(p, t)) return;
+    if (t.rows <= 0) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t K = p.K, KB = p.KB;
+
+    // Each range covers only this tile's rows (<= 2^31 bytes since K <= 2^23),
+    // so kOobOffset always lies past it.
+    const int64_t wrows = p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * KB, clamp_bytes(t.rows * KB * 4));
+
+    // Per-lane load descriptors.  Load piece q (1 KB) covers tile rows
+    // [8q, 8q+8); lane i lands at LDS row 8q + i/8, 16-byte slot i%8, which
+    // holds K chunk c = slot ^ swz(row), swz(r) = (r & 7) ^ ((r >> 3) & 1).
+    const int r_in = lane >> 3;
+    uint32_t wgo[C::kWLoads], xgo[C::kXLoads];   // global offset at kb = 0
+    int wchunk[C::kWLoads], xchunk[C::kXLoads];
+#pragma unroll
+    for (int j = 0; j < C::kWLoads; ++j) {
+        const int q = wave + j * C::kWaves;
+        const int c = (lane & 7) ^ r_in ^ (q & 1);
+        wchunk[j] = c;
+        wgo[j] = (uint32_t)((8 * q + r_in) * K + 16 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < C::kXLoads; ++j) {
+        const int q = wave + j * C::kWaves;
+        const int c = (lane & 7) ^ r_in ^ (q & 1);
+        xchunk[j] = c;
+        xgo[j] = (uint32_t)((8 * q + r_in) * K + 16 * c);
+    }
+    const bool loads_scales = wave < WM;
+
+    // Issue one stage's buffer->LDS loads for K block kb.  A chunk at or past
+    // K (the K tail, and every chunk of a block kb >= KB) reads as zero.  The
+    // scale piece of a block kb >= KB is clamped to the last block: that stage
+    // is never consumed.
+    auto issue = [&](char *stage, int64_t kb) {
+        const int64_t k0 = kb * kBlock;
+        const uint32_t kofs = (uint32_t)k0;
+#pragma unroll
+        for (int j = 0; j < C::kWLoads; ++j) {
+            const int q = wave + j * C::kWaves;
+            const uint32_t off = (k0 + 16 * wchunk[j] < K) ? wgo[j] + kofs : kOobOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (BI8_LDS void *)(stage + C::kWOff + q * 1024), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < C::kXLoads; ++j) {
+            const int q = wave + j * C::kWaves;
+            const uint32_t off = (k0 + 16 * xchunk[j] < K) ? xgo[j] + kofs : kOobOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (BI8_LDS void *)(stage + C::kXOff + q * 1024), 16, off, 0, 0, 0);
+        }
+        if (loads_scales) {
+            const int64_t r = 64 * wave + lane;
+            const int64_t kbc = kb < KB ? kb : KB - 1;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                sr, (BI8_LDS void *)(stage + C::kSOff + 256 * wave), 4,
+                (uint32_t)((r * KB + kbc) * 4), 0, 0, 0);
+        }
+    };
+
+    // Fragment read addresses (32x32x32 operand layout: lane -> row lane & 31,
+    // 16-byte K chunk 2*s + (lane >> 5) for k-step s).
+    const int wn = wave % WN, wm = wave / WN;
+    const int rr = lane & 31, hi = lane >> 5;
+    const int swz = (rr & 7) ^ ((rr >> 3) & 1);
+    int frag_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
+    const int wrow0 = C::kWOff + (wn * 64 + rr) * 128;
+    const int xrow0 = C::kXOff + (wm * 64 + rr) * 128;
+    const int srow0 = C::kSOff + (wm * 64 + rr) * 4;
+
+    int64_t nbw = (t.n0 + wn * 64) / kBlock;
+    if (nbw > p.NB - 1) nbw = p.NB - 1;
+    const float *ws_row = t.ws + nbw * KB;
+
+    i32x16 zero16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) zero16[i] = 0;
+    f32x16 y[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[a][b][i] = 0.f;
+
+    auto compute = [&](const char *stage, int64_t kb) {
+        i32x4 wf[2][4], xf[2][4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                wf[a][s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
+        const float xs0 = *reinterpret_cast<const float *>(stage + srow0);
+        const float xs1 = *reinterpret_cast<const float *>(stage + srow0 + 32 * 4);
+        const float wsv = ws_row[kb];
+        const float tb[2] = {xs0 * wsv, xs1 * wsv};
+        // Sub-tile by sub-tile: a chain of 4 accumulating MFMAs over the block,
+        // then its rescale, which can overlap the next sub-tile's chain.
+#pragma unroll
+        for (int ab = 0; ab < 4; ++ab) {
+            const int a = ab >> 1, b = ab & 1;
+            i32x16 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a][0], xf[b][0], zero16, 0, 0, 0);
+#pragma unroll
+            for (int s = 1; s < 4; ++s)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a][s], xf[b][s], acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[a][b][i] = fmaf((float)acc[i], tb[b], y[a][b][i]);
+        }
+        // The rescale of this block must finish inside its step: without this
+        // the optimiser sinks it into later steps and keeps several blocks'
+        // int32 accumulators alive.
+        asm volatile("" : "+v"(y[0][0]), "+v"(y[0][1]), "+v"(y[1][0]), "+v"(y[1][1]));
+    };
+
+    // 3-stage ring: stage kb lives in lds[kb % 3]; loads run two steps ahead.
+    auto step = [&](char *cur, char *ahead, int64_t kb) {
+        if (loads_scales)
+            wait_vmcnt<C::kTileLoads + 1>();
+        else
+            wait_vmcnt<C::kTileLoads>();
+        lds_barrier();
+        issue(ahead, kb + 2);
+        compute(cur, kb);
+        // keep each block's MFMAs and rescale inside its own step (bounds the
+        // live accumulators)
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(lds0, 0);
+    issue(lds1, 1);
+    int64_t kb = 0;
+    for (; kb + 3 <= KB; kb += 3) {
+        step(lds0, lds2, kb);
+        step(lds1, lds0, kb + 1);
+        step(lds2, lds1, kb + 2);
+    }
+    if (kb < KB) step(lds0, lds2, kb++);
+    if (kb < KB) step(lds1, lds0, kb++);
+    wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
+
+    // Store.  32x32 result layout: lane -> token column (lane & 31); element i
+    // -> weight row 8 * (i / 4) + 4 * (lane >> 5) + (i % 4).
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t ml = wm * 64 + b * 32 + rr;
+        if (ml >= t.rows) continue;
+        uint16_t *yrow = p.y + (t.m0 + ml) * p.N;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t n = t.n0 + wn * 64 + a * 32 + 8 * i4 + 4 * hi;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = y[a][b][4 * i4 + e];
+                    if (p.bias && n + e < p.N) v[e] += bf16_bits_to_f32(p.bias[n + e]);
+                }
+                if (p.wide_store) {
+                    if (n < p.N) {
+                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                }
+            }
+        }
+    }
+}
+
+template <int WN, int WM, bool MOE>
+hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
+    using C = TileCfg<WN, WM>;
+    const int64_t total = p.tiles_m * p.tiles_n;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, MOE>), dim3((unsigned)total), dim3(C::kThreads),
+                       0, stream, p);
+    return hipGetLastError();
+}
+
+GemmArgs make_args(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                   const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K) {
+    GemmArgs p{};
+    p.xq = xq;
+    p.xs = xs;
+    p.w = w;
+    p.ws = ws;
+    p.bias = bias;
+    p.y = y;
+    p.offsets = nullptr;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.KB = (K + kBlock - 1) / kBlock;
+    p.NB = (N + kBlock - 1) / kBlock;
+    p.E = 1;
+    p.wide_store = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 7) == 0);
+    return p;
+}
+
+}  // namespace
+
+GemmPath select_gemm_path(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    if (M <= 32) return GemmPath::kSkinny;
+    const int64_t large_tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    return large_tiles >= 256 ? GemmPath::kTiledLarge : GemmPath::kTiledSmall;
+}
+
+hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const int8_t *w,
+                       const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
+                       int64_t K, hipStream_t stream) {
+    GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
+    switch (path) {
+        case GemmPath::kSkinny: {
+            if (M > 32) return hipErrorInvalidValue;
+            const int64_t tiles = (N + 15) / 16;
+            if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
+            const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
+            if (M <= 16)
+                hipLaunchKernelGGL(gemm_skinny_kernel<1>, dim3((unsigned)tiles),
+                                   dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
+            else
+                hipLaunchKernelGGL(gemm_skinny_kernel<2>, dim3((unsigned)tiles),
+                                   dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
+            return hipGetLastError();
+        }
+        case GemmPath::kTiledLarge:
+            p.tiles_m = (M + 127) / 128;
+            p.tiles_n = (N + 255) / 256;
+            return launch_tiled<4, 2, false>(p, stream);
+        case GemmPath::kTiledSmall:
+            p.tiles_m = (M + 63) / 64;
+            p.tiles_n = (N + 127) / 128;
+            return launch_tiled<2, 1, false>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_moe_gemm(const int8_t *xq, const float *xs, const int32_t *offsets,
+                           const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
+                           int64_t K, int32_t E, hipStream_t stream) {
+    GemmArgs p = make_args(xq, xs, w, ws, nullptr, y, R, N, K);
+    p.offsets = offsets;
+    p.E = E;
+    p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
+    p.tiles_n = (N + 255) / 256;
+    return launch_tiled<4, 2, true>(p, stream);
+}
+
+}  // namespace bi8

@@ -1,0 +1,144 @@
+/*
+ * blockint8.h -- C ABI of the block-wise INT8 W8A8 linear layer for AMD
+ * Instinct MI355X (gfx950, CDNA4).
+ *
+ * The method (page "[SGLang] Block-wise INT8: 블록 단위 정수 양자화",
+ * blog.secrett2633.cloud):
+ *   - weights are int8 [N, K] (output dim first) with one fp32 scale per
+ *     block_n x block_k block, scale tensor [ceil(N/block_n), ceil(K/block_k)]
+ *     (structure diagram; section 2 and its worked example);
+ *   - activations are quantised at run time, per token, with no static input
+ *     scale (section 4; section 1 allows only the dynamic scheme); one fp32
+ *     scale per (token, group of block_k consecutive K entries);
+ *   - the GEMM multiplies int8 by int8, sums exactly inside each K block and
+ *     rescales each block sum by activation scale x weight scale in fp32
+ *     (design rationale item 3: fp32 scales, multiplied on dequantisation);
+ *   - the MoE form keeps one int8 weight and one scale tensor per expert on a
+ *     leading expert axis (sections 5 and 6).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     owned by the caller; tensors are row-major and dense unless a leading
+ *     dimension is given.  bf16 values are passed as their uint16_t bits.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; nothing is synchronised.
+ *   - The library allocates no device memory and keeps no state between
+ *     calls apart from a thread-local error message.
+ *   - Every argument is checked on the host before any HIP call; a failed
+ *     check returns a status below and enqueues nothing.  BI8_ERR_HIP means a
+ *     HIP call (the launch) failed; see blockint8_last_error().
+ *   - This library implements the [128, 128] block, the block the pages
+ *     describe as the usual one (design rationale item 1); any other positive
+ *     block size returns BI8_ERR_BLOCK.
+ *   - K must be a multiple of 16 (int8 rows are moved in 16-byte pieces);
+ *     N and M are arbitrary.  Empty inputs (M == 0, R == 0) are a no-op.
+ */
+#ifndef BLOCKINT8_H_
+#define BLOCKINT8_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bi8_status {
+    BI8_OK = 0,
+    BI8_ERR_NULL = 1,   /* a required pointer is NULL                          */
+    BI8_ERR_SHAPE = 2,  /* a size is out of range (negative, zero, ldx < K, ...) */
+    BI8_ERR_BLOCK = 3,  /* block size not positive, or not [128, 128]           */
+    BI8_ERR_ALIGN = 4,  /* pointer / leading dimension / K alignment violated   */
+    BI8_ERR_HIP = 5     /* a HIP runtime call failed                            */
+} bi8_status;
+
+/* Largest K accepted (elements); M, N and R are bounded by 2^31 - 1. */
+#define BI8_MAX_K (1 << 23)
+
+/* Static, never-NULL name of a status code. */
+const char *blockint8_status_string(int32_t status);
+
+/* Human-readable detail of the last failing call made on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char *blockint8_last_error(void);
+
+/*
+ * Dynamic activation quantisation (section 4: per-token scales computed at
+ * run time; design rationale item 3: int8 values, fp32 scales).
+ *
+ *   x   bf16 [M, ldx], the first K columns of each row are quantised
+ *   xq  int8 [M, K]                    (output)
+ *   xs  fp32 [M, ceil(K / block_k)]    (output)
+ *
+ * For token m and group g (columns [g*block_k, min(K, (g+1)*block_k))):
+ *   amax = max |x|,  s = amax / 127 (binary32, round to nearest),
+ *   xq = 0 if s == 0 else clamp(round_half_even(x / s), -127, 127),
+ *   xs[m, g] = s.
+ * Bit-exact for finite inputs (divisions are correctly rounded, subnormals
+ * are kept).  Non-finite inputs give unspecified codes.
+ *
+ * Errors: NULL x/xq/xs (M > 0) -> BI8_ERR_NULL; M < 0, K <= 0, K > BI8_MAX_K,
+ * ldx < K -> BI8_ERR_SHAPE; block_k != 128 -> BI8_ERR_BLOCK; K % 16,
+ * ldx % 8, x / xq not 16-byte aligned, xs not 4-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                            int32_t block_k, int8_t *xq, float *xs, void *stream);
+
+/*
+ * Block-scaled int8 GEMM, y = x . W^T (structure diagram and section 2: int8
+ * weight [N, K] with fp32 block scales; section 4: the linear's inputs are
+ * the weight, its block scales, dynamic activation scales and an optional
+ * bias).
+ *
+ *   xq    int8 [M, K]                         (from blockint8_quant_act)
+ *   xs    fp32 [M, ceil(K / block_k)]
+ *   w     int8 [N, K]
+ *   ws    fp32 [ceil(N / block_n), ceil(K / block_k)]
+ *   bias  bf16 [N] or NULL
+ *   y     bf16 [M, N]                         (output)
+ *
+ *   y[m, n] = bf16_rne( sum_g  (sum_{k in g} xq[m,k] * w[n,k])
+ *                              * (xs[m, g] * ws[n / block_n, g])  (+ bias[n]) )
+ * Block sums are exact int32; the rescaled sum is accumulated in fp32 (the
+ * order of the fp32 additions is unspecified).
+ *
+ * Errors: NULL xq/xs/w/ws/y (M > 0) -> BI8_ERR_NULL; M < 0, N <= 0, K <= 0,
+ * K > BI8_MAX_K -> BI8_ERR_SHAPE; blocks != [128, 128] -> BI8_ERR_BLOCK;
+ * K % 16, xq / w not 16-byte aligned, xs / ws not 4-byte aligned, y / bias
+ * not 2-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                       const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                       int32_t block_n, int32_t block_k, void *stream);
+
+/*
+ * Grouped (FusedMoE) block-scaled int8 GEMM (section 5: per-expert int8
+ * weights with per-expert fp32 block scales on a leading expert axis;
+ * section 6: the MoE runner applies the int8 W8A8 block arithmetic per
+ * expert).  Rows are the dispatched tokens, sorted by expert.
+ *
+ *   xq              int8 [R, K]
+ *   xs              fp32 [R, ceil(K / block_k)]
+ *   expert_offsets  int32 [E + 1] on the DEVICE: rows [off[e], off[e+1]) use
+ *                   expert e.  Precondition (not read by the host, so not
+ *                   checked): off[0] = 0, off[E] = R, non-decreasing.
+ *   w               int8 [E, N, K]
+ *   ws              fp32 [E, ceil(N / block_n), ceil(K / block_k)]
+ *   y               bf16 [R, N]               (output)
+ *
+ * Each segment is blockint8_gemm with that expert's w[e], ws[e] (no bias).
+ * Empty segments are allowed.
+ *
+ * Errors: as blockint8_gemm; NULL expert_offsets -> BI8_ERR_NULL;
+ * E <= 0 or E > 65536, R < 0 -> BI8_ERR_SHAPE; expert_offsets not 4-byte
+ * aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
+                           const int8_t *w, const float *ws, uint16_t *y,
+                           int64_t R, int64_t N, int64_t K, int32_t E,
+                           int32_t block_n, int32_t block_k, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKINT8_H_ */

@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI library (no GPU needed, no compute launched).
+
+The library must load, export every function ``include/blockint8.h``
+declares, and reject every bad argument on the host before any HIP call, with
+the documented status.  Calls here never pass a valid argument set, so no
+kernel is ever launched (fake pointers are used only where the call is
+rejected first).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_wise_int8_amd as bi8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blockint8.h")
+
+OK, NULL, SHAPE, BLOCK, ALIGN, HIP = 0, 1, 2, 3, 4, 5
+P16 = 0x10000          # fake, 16-byte aligned "device" address (never dereferenced)
+P_ODD = 0x10001
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(blockint8_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bi8.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"blockint8_status_string", "blockint8_last_error",
+                          "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm"}
+    for name in names:
+        assert hasattr(lib, name), name
+    # exported with C linkage (no mangling) in the shared object
+    raw = ctypes.CDLL(bi8.lib_path())
+    for name in names:
+        getattr(raw, name)
+
+
+def test_status_strings(lib):
+    for code, name in [(OK, "BI8_OK"), (NULL, "BI8_ERR_NULL"), (SHAPE, "BI8_ERR_SHAPE"),
+                       (BLOCK, "BI8_ERR_BLOCK"), (ALIGN, "BI8_ERR_ALIGN"), (HIP, "BI8_ERR_HIP")]:
+        assert lib.blockint8_status_string(code).decode() == name
+    assert lib.blockint8_status_string(99).decode() == "BI8_ERR_UNKNOWN"
+
+
+def quant(lib, x=P16, M=4, K=256, ldx=256, bk=128, xq=P16, xs=P16):
+    return lib.blockint8_quant_act(x, M, K, ldx, bk, xq, xs, None)
+
+
+def gemm(lib, xq=P16, xs=P16, w=P16, ws=P16, bias=None, y=P16, M=4, N=256, K=256, bn=128, bk=128):
+    return lib.blockint8_gemm(xq, xs, w, ws, bias, y, M, N, K, bn, bk, None)
+
+
+def moe(lib, xq=P16, xs=P16, off=P16, w=P16, ws=P16, y=P16, R=4, N=256, K=256, E=2, bn=128, bk=128):
+    return lib.blockint8_moe_gemm(xq, xs, off, w, ws, y, R, N, K, E, bn, bk, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), NULL), (dict(xq=None), NULL), (dict(xs=None), NULL),
+    (dict(M=-1), SHAPE), (dict(K=0), SHAPE), (dict(K=-16), SHAPE), (dict(K=1 << 24, ldx=1 << 24), SHAPE),
+    (dict(ldx=128), SHAPE),
+    (dict(bk=64), BLOCK), (dict(bk=0), BLOCK), (dict(bk=-128), BLOCK),
+    (dict(K=200, ldx=200), ALIGN), (dict(ldx=260), ALIGN), (dict(x=P_ODD), ALIGN),
+    (dict(xq=P16 + 8), ALIGN), (dict(xs=P16 + 2), ALIGN),
+])
+def test_quant_rejects(lib, kw, status):
+    assert quant(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_quant_act")
+
+
+def test_quant_empty_is_noop(lib):
+    assert quant(lib, M=0, x=None, xq=None, xs=None) == OK
+    assert lib.blockint8_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xq=None), NULL), (dict(xs=None), NULL), (dict(w=None), NULL), (dict(ws=None), NULL),
+    (dict(y=None), NULL),
+    (dict(M=-1), SHAPE), (dict(N=0), SHAPE), (dict(N=-5), SHAPE), (dict(K=0), SHAPE),
+    (dict(M=1 << 31), SHAPE), (dict(K=1 << 24), SHAPE),
+    (dict(bn=0), BLOCK), (dict(bk=-1), BLOCK), (dict(bn=64), BLOCK), (dict(bk=256), BLOCK),
+    (dict(bn=1, bk=256), BLOCK),
+    (dict(K=4008), ALIGN), (dict(xq=P16 + 4), ALIGN), (dict(w=P16 + 8), ALIGN),
+    (dict(xs=P16 + 1), ALIGN), (dict(ws=P16 + 3), ALIGN), (dict(y=P_ODD), ALIGN),
+    (dict(bias=P_ODD), ALIGN),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert gemm(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_gemm")
+
+
+def test_gemm_empty_is_noop(lib):
+    assert gemm(lib, M=0, xq=None, xs=None, w=None, ws=None, y=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(off=None), NULL), (dict(w=None), NULL), (dict(xq=None), NULL),
+    (dict(E=0), SHAPE), (dict(E=-1), SHAPE), (dict(E=65537), SHAPE), (dict(R=-1), SHAPE),
+    (dict(N=0), SHAPE),
+    (dict(bn=64), BLOCK),
+    (dict(K=100), ALIGN), (dict(off=P16 + 2), ALIGN), (dict(xq=P16 + 4), ALIGN),
+])
+def test_moe_rejects(lib, kw, status):
+    assert moe(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_moe_gemm")
+
+
+def test_moe_empty_is_noop(lib):
+    assert moe(lib, R=0, xq=None, xs=None, off=None, w=None, ws=None, y=None) == OK
+
+
+def test_binding_has_no_cpu_path():
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        bi8.quant_act(x)
+    xq = torch.zeros((4, 128), dtype=torch.int8)
+    xs = torch.zeros((4, 1), dtype=torch.float32)
+    w = torch.zeros((8, 128), dtype=torch.int8)
+    ws = torch.zeros((1, 1), dtype=torch.float32)
+    with pytest.raises(ValueError, match="HIP device"):
+        bi8.gemm(xq, xs, w, ws)
+    with pytest.raises(ValueError, match="HIP device"):
+        bi8.moe_gemm(xq, xs, torch.zeros(2, dtype=torch.int32), w[None], ws[None])
+
+
+def test_scale_shape_helper():
+    assert bi8.scale_shape(4096, 4096) == (32, 32)
+    assert bi8.scale_shape(5000, 4000) == (40, 32)

@@ -1,0 +1,272 @@
+"""Parity of the HIP path with the CPU oracle, element by element.
+
+Quantisation (codes and scales) must match bit-exactly; GEMM outputs must be
+within max-relative error 1e-2 of the output magnitude (``GEMM_REL_TOL``).
+Integer-valued and power-of-two cases, whose fp32 sums are exact in any
+order, must match bit-exactly.  At the full workload sizes, the oracle
+computes sampled rows (all N columns of each sampled row), and the GPU runs in
+the same launch configuration the benchmark times (the library picks the
+kernel from the shape).
+
+Page cited: "[SGLang] Block-wise INT8: 블록 단위 정수 양자화" (blog.secrett2633.cloud).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_wise_int8_amd as bi8
+import oracle
+import workloads as wl
+from gpu_util import (assert_gemm_close, bf16_bits, bf16_to_dev, device, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_quant(x_bits):
+    xq, xs = bi8.quant_act(bf16_to_dev(x_bits))
+    return xq.cpu().numpy(), xs.cpu().numpy()
+
+
+def make_case(seed, M, N, K, outlier_frac=0.0):
+    rng = wl.rng_for(seed)
+    x = wl.activations(rng, M, K, outlier_frac)
+    w = wl.weights(rng, N, K)
+    NB, KB = oracle.scale_shape(N, K)
+    ws = wl.weight_scales(rng, NB, KB)
+    return x, w, ws
+
+
+def sample_rows(M, n, rng):
+    """Rows spread over the whole range, always including the first and last."""
+    if M <= n:
+        return np.arange(M)
+    inner = rng.choice(np.arange(1, M - 1), n - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], inner]))
+
+
+# ------------------------------------------------------------------ quant --
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "ragged", "down"])
+def test_quant_bit_exact_workloads(name):
+    c = wl.CONFIGS[name]
+    x = wl.activations(wl.rng_for(c["seed"]), c["M"], c["K"], c.get("outlier_frac", 0.0))
+    q_ref, s_ref = oracle.quant_act(x)
+    q, s = gpu_quant(x)
+    assert np.array_equal(q, q_ref)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quant_special_values_bit_exact():
+    rows = []
+    rows.append([127.0, 0.5, 1.5, 2.5, -2.5, 126.5, -0.5, 3.5] + [0.0] * 120)   # RNE ties, s = 1
+    rows.append([0.0] * 128)                                                     # zero group
+    rows.append([1.484375, -0.7421875] + [0.0] * 126)                            # x/s == -63.5 tie
+    rows.append([6.96875, 3.484375] + [0.0] * 126)
+    x = wl.to_bf16_bits(np.array(rows, np.float32))
+    sub = np.zeros((1, 128), np.uint16)
+    sub[0, :4] = [0x0001, 0x0003, 0x8002, 0x007F]                                # subnormal group
+    x = np.concatenate([x, sub])
+    q_ref, s_ref = oracle.quant_act(x)
+    q, s = gpu_quant(x)
+    assert np.array_equal(q, q_ref) and np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert q[0, :8].tolist() == [127, 0, 2, 2, -2, 126, 0, 4]
+    assert s[1, 0] == 0.0 and not q[1].any()
+    assert 0 < s[4, 0] < np.finfo(np.float32).tiny
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (5, 144), (7, 4000), (64, 128), (2, 14336),
+                                 (65537, 128)])
+def test_quant_shapes_bit_exact(M, K):
+    rng = np.random.default_rng(M * 7 + K)
+    x = wl.activations(rng, M, K, 0.02)
+    q_ref, s_ref = oracle.quant_act(x)
+    q, s = gpu_quant(x)
+    assert np.array_equal(q, q_ref) and np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_quant_row_stride():
+    rng = np.random.default_rng(21)
+    M, K, ldx = 9, 384, 520
+    full = wl.activations(rng, M, ldx)
+    xd = bf16_to_dev(full)[:, :K]
+    assert xd.stride(0) == ldx
+    xq, xs = bi8.quant_act(xd)
+    q_ref, s_ref = oracle.quant_act(full, K=K)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------- gemm --
+
+def run_gemm(xq, xs, w, ws, bias=None):
+    y = bi8.gemm(to_dev(xq), to_dev(xs), to_dev(w), to_dev(ws),
+                 None if bias is None else bf16_to_dev(bias))
+    return bf16_bits(y)
+
+
+SHAPES = [
+    # skinny path (M <= 32)
+    (1, 16, 16), (1, 256, 256), (8, 4096, 512), (8, 100, 4000), (16, 300, 144), (17, 257, 1040),
+    (32, 512, 384), (5, 1000, 4096),
+    # tiled small and large paths, ragged N / K / M
+    (33, 256, 256), (64, 128, 128), (100, 1000, 272), (129, 384, 400), (333, 500, 4000),
+    (256, 2048, 256), (300, 5000, 128), (200, 7, 128), (1000, 16, 64), (513, 1024, 1024),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_shapes_vs_oracle(M, N, K):
+    x, w, ws = make_case((M, N, K), M, N, K)
+    xq, xs = oracle.quant_act(x)
+    y_ref = oracle.gemm(xq, xs, w, ws)
+    y = run_gemm(xq, xs, w, ws)
+    assert_gemm_close(y, y_ref, "M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "ragged", "prefill", "gate_up", "down"])
+def test_gemm_workloads_vs_oracle(name):
+    c = wl.CONFIGS[name]
+    M, N, K = c["M"], c["N"], c["K"]
+    x, w, ws = make_case(c["seed"], M, N, K, c.get("outlier_frac", 0.0))
+    xq_d, xs_d = bi8.quant_act(bf16_to_dev(x))
+    y = bf16_bits(bi8.gemm(xq_d, xs_d, to_dev(w), to_dev(ws)))
+    xq, xs = xq_d.cpu().numpy(), xs_d.cpu().numpy()
+    rows = sample_rows(M, 12 if N * K > 2 ** 26 else 24, np.random.default_rng(5))
+    q_ref, s_ref = oracle.quant_act(x[rows])
+    assert np.array_equal(xq[rows], q_ref) and np.array_equal(xs[rows], s_ref)
+    y_ref = oracle.gemm(q_ref, s_ref, w, ws)
+    assert_gemm_close(y[rows], y_ref, name)
+    assert np.all(np.isfinite(y.view(np.int16).astype(np.float64)))
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 512, 1024), (24, 300, 1040), (200, 520, 1024), (333, 260, 896)])
+def test_gemm_integer_closed_form_bit_exact(M, N, K):
+    """Unit scales and integer activations: y == bf16(int64 matmul) exactly."""
+    rng = np.random.default_rng(M + N + K)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    w = wl.weights(rng, N, K)
+    NB, KB = oracle.scale_shape(N, K)
+    xs = np.ones((M, KB), np.float32)
+    ws = np.ones((NB, KB), np.float32)
+    exact = (xq.astype(np.int64) @ w.astype(np.int64).T).astype(np.float32)
+    y = run_gemm(xq, xs, w, ws)
+    assert np.array_equal(y, wl.to_bf16_bits(exact))
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 300, 520), (150, 600, 520)])
+def test_gemm_power_of_two_bit_exact(M, N, K):
+    """Power-of-two scales, |xq| <= 31: every partial sum exact in fp32."""
+    rng = np.random.default_rng(10 + M)
+    NB, KB = oracle.scale_shape(N, K)
+    xq = rng.integers(-31, 32, (M, K), dtype=np.int8)
+    w = wl.weights(rng, N, K)
+    xs = np.exp2(rng.integers(-8, -6, (M, KB))).astype(np.float32)
+    ws = np.exp2(rng.integers(-6, -4, (NB, KB))).astype(np.float32)
+    y = run_gemm(xq, xs, w, ws)
+    assert np.array_equal(y, oracle.gemm(xq, xs, w, ws))
+
+
+@pytest.mark.parametrize("M", [4, 96])
+def test_gemm_bias(M):
+    N, K = 384, 256
+    x, w, ws = make_case(99 + M, M, N, K)
+    bias = wl.activations(np.random.default_rng(1), 1, N)[0]
+    xq, xs = oracle.quant_act(x)
+    y = run_gemm(xq, xs, w, ws, bias)
+    assert_gemm_close(y, oracle.gemm(xq, xs, w, ws, bias=bias), "bias")
+
+
+def test_linear_pipeline_matches_oracle():
+    M, N, K = 40, 640, 768
+    x, w, ws = make_case(31, M, N, K, 0.01)
+    y = bf16_bits(bi8.linear(bf16_to_dev(x), to_dev(w), to_dev(ws)))
+    xq, xs = oracle.quant_act(x)
+    assert_gemm_close(y, oracle.gemm(xq, xs, w, ws), "linear")
+
+
+def test_gemm_unaligned_output_rows():
+    """N % 4 != 0 takes the element-wise store path."""
+    M, N, K = 70, 333, 256
+    x, w, ws = make_case(41, M, N, K)
+    xq, xs = oracle.quant_act(x)
+    assert_gemm_close(run_gemm(xq, xs, w, ws), oracle.gemm(xq, xs, w, ws), "N=333")
+
+
+def test_gemm_empty_and_errors():
+    dev = device()
+    xq = torch.zeros((0, 128), dtype=torch.int8, device=dev)
+    xs = torch.zeros((0, 1), dtype=torch.float32, device=dev)
+    w = torch.zeros((8, 128), dtype=torch.int8, device=dev)
+    ws = torch.ones((1, 1), dtype=torch.float32, device=dev)
+    assert bi8.gemm(xq, xs, w, ws).shape == (0, 8)
+    with pytest.raises(bi8.BlockInt8Error, match="BI8_ERR_BLOCK"):
+        bi8.gemm(xq, xs, w, ws, block=(64, 128))
+
+
+# -------------------------------------------------------------------- moe --
+
+def moe_case(seed, counts, N, K):
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    x = wl.activations(rng, R, K)
+    w = wl.weights(rng, E, N, K)
+    NB, KB = oracle.scale_shape(N, K)
+    ws = wl.weight_scales(rng, E, NB, KB)
+    return x, off, w, ws
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([40], 256, 256),
+    ([7, 0, 130, 1, 0, 257], 300, 400),
+    ([0, 0, 128], 128, 128),
+    ([300, 5, 33, 128, 129], 512, 1024),
+])
+def test_moe_small_vs_oracle(counts, N, K):
+    x, off, w, ws = moe_case(len(counts) * 100 + N, counts, N, K)
+    xq, xs = oracle.quant_act(x)
+    y_ref = oracle.moe_gemm(xq, xs, off, w, ws)
+    y = bf16_bits(bi8.moe_gemm(to_dev(xq), to_dev(xs), to_dev(off), to_dev(w), to_dev(ws)))
+    assert_gemm_close(y, y_ref, "moe %s" % counts)
+
+
+def test_moe_one_expert_equals_dense_gemm():
+    x, off, w, ws = moe_case(7, [500], 640, 512)
+    xq, xs = to_dev(oracle.quant_act(x)[0]), to_dev(oracle.quant_act(x)[1])
+    y_moe = bf16_bits(bi8.moe_gemm(xq, xs, to_dev(off), to_dev(w), to_dev(ws)))
+    y_dense = bf16_bits(bi8.gemm(xq, xs, to_dev(w[0]), to_dev(ws[0])))
+    assert np.array_equal(y_moe, y_dense)
+
+
+def test_moe_workload_vs_oracle():
+    """The MoE workload: 4096 tokens, top-2 of 8 experts, w13 then w2."""
+    c = wl.CONFIGS["moe"]
+    T, H, I, E, k = c["T"], c["H"], c["I"], c["E"], c["topk"]
+    rng = wl.rng_for(c["seed"])
+    x = wl.activations(rng, T, H)
+    logits = wl.router_logits(rng, T, E)
+    tok, _, off = wl.dispatch_topk(logits, k)
+    w13 = wl.weights(rng, E, 2 * I, H)
+    ws13 = wl.weight_scales(rng, E, *oracle.scale_shape(2 * I, H))
+    w2 = wl.weights(rng, E, H, I)
+    ws2 = wl.weight_scales(rng, E, *oracle.scale_shape(H, I))
+    x2 = wl.activations(rng, T * k, I)          # stand-in for the activated w13 output
+
+    dev_off = to_dev(off)
+    xq1, xs1 = bi8.quant_act(bf16_to_dev(x[tok]))
+    y13 = bf16_bits(bi8.moe_gemm(xq1, xs1, dev_off, to_dev(w13), to_dev(ws13)))
+    xq2, xs2 = bi8.quant_act(bf16_to_dev(x2))
+    y2 = bf16_bits(bi8.moe_gemm(xq2, xs2, dev_off, to_dev(w2), to_dev(ws2)))
+
+    srng = np.random.default_rng(3)
+    for e in range(E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        rows = a + sample_rows(b - a, 3, srng)
+        q1, s1 = oracle.quant_act(x[tok[rows]])
+        assert np.array_equal(xq1.cpu().numpy()[rows], q1)
+        assert_gemm_close(y13[rows], oracle.gemm(q1, s1, w13[e], ws13[e]), "w13 e=%d" % e)
+        q2, s2 = oracle.quant_act(x2[rows])
+        assert_gemm_close(y2[rows], oracle.gemm(q2, s2, w2[e], ws2[e]), "w2 e=%d" % e)
