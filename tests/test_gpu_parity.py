@@ -153,9 +153,12 @@ def test_gemm_integer_closed_form_bit_exact(M, N, K):
     assert np.array_equal(y, wl.to_bf16_bits(exact))
 
 
-@pytest.mark.parametrize("M,N,K", [(7, 300, 520), (150, 600, 520)])
+@pytest.mark.parametrize("M,N,K", [(7, 300, 528), (150, 600, 528)])
 def test_gemm_power_of_two_bit_exact(M, N, K):
-    """Power-of-two scales, |xq| <= 31: every partial sum exact in fp32."""
+    """Power-of-two scales, |xq| <= 31: every partial sum exact in fp32.
+
+    5 K blocks (the last 16 wide); block sums < 2^19, scale products within a
+    factor 4, so every partial sum has fewer than 24 significant bits."""
     rng = np.random.default_rng(10 + M)
     NB, KB = oracle.scale_shape(N, K)
     xq = rng.integers(-31, 32, (M, K), dtype=np.int8)
