@@ -66,14 +66,16 @@ def quant_bytes(M, K):
     return 2 * M * K + M * K + 4 * M * bi8.scale_shape(1, K)[1]
 
 
-def n_copies(weight_bytes):
+def n_copies(weight_bytes, override=None):
+    if override:
+        return int(override)
     return int(max(1, min(MAX_COPIES, -(-ROTATE_BYTES // max(weight_bytes, 1)))))
 
 
 class Dense:
     """quant_act + gemm on one [M, K] x [N, K] linear."""
 
-    def __init__(self, name):
+    def __init__(self, name, copies=None):
         c = wl.CONFIGS[name]
         self.name = name
         self.M, self.N, self.K = c["M"], c["N"], c["K"]
@@ -83,7 +85,7 @@ class Dense:
         self.ws_np = wl.weight_scales(rng, *bi8.scale_shape(self.N, self.K))
         self.x = bf16_dev(self.x_np)
         w, ws = dev(self.w_np), dev(self.ws_np)
-        self.copies = n_copies(self.N * self.K)
+        self.copies = n_copies(self.N * self.K, copies)
         self.w = [w] + [w.clone() for _ in range(self.copies - 1)]
         self.ws = [ws] + [ws.clone() for _ in range(self.copies - 1)]
         KB = bi8.scale_shape(self.N, self.K)[1]
@@ -208,8 +210,8 @@ class Moe:
         return ops / dt / 1e12, "%d rows of expert 0, w13 projection, quant+GEMM, %.1f s" % (rows, dt)
 
 
-def make_workload(name):
-    return Moe() if name == "moe" else Dense(name)
+def make_workload(name, copies=None):
+    return Moe() if name == "moe" else Dense(name, copies)
 
 
 def capture(fn, steps):
@@ -271,6 +273,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="weight copies to rotate over (default: enough to exceed the Infinity Cache)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -285,7 +289,7 @@ def main():
 
     bi8.load()
     log("[bench] setting up workload %s" % args.workload)
-    w = make_workload(args.workload)
+    w = make_workload(args.workload, args.copies)
     use_graph = not args.eager
 
     log("[bench] warmup %d steps" % args.warmup)

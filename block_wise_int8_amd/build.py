@@ -74,8 +74,19 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
+    check_symbols(tmp)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def check_symbols(path: str) -> None:
+    """Fail the build if the library references a symbol of its own that no
+    object defines (e.g. a kernel launch stub the host pass did not emit)."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    out = subprocess.run([nm, "-u", path], check=True, capture_output=True, text=True).stdout
+    missing = [l.split()[-1] for l in out.splitlines() if "bi8" in l or "blockint8" in l]
+    if missing:
+        raise RuntimeError("libblockint8.so has undefined internal symbols: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

@@ -13,6 +13,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define BI8_LDS __attribute__((address_space(3)))
+#define BI8_CONST __attribute__((address_space(4)))
 
 // The [128, 128] block this library implements.
 constexpr int kBlock = 128;

@@ -172,10 +172,12 @@ struct TileCfg {
     static constexpr int kWOff = 0;                  // LDS layout of one stage
     static constexpr int kXOff = kBN * 128;
     static constexpr int kSOff = kXOff + kBM * 128;
-    static constexpr int kStageBytes = kSOff + kBM * 4;
+    static constexpr int kStageBytes = kSOff + kWaves * 256;   // one 256 B scale slot per wave
     static constexpr int kWLoads = 8 / WM;           // 1 KB W pieces per wave per stage
     static constexpr int kXLoads = 8 / WN;           // 1 KB X pieces per wave per stage
     static constexpr int kTileLoads = kWLoads + kXLoads;
+    static constexpr int kScaleRowsPerWave = kBM / kWaves;   // one activation-scale DMA per wave
+    static constexpr int kLoads = kTileLoads + 1;            // loads per wave per stage
     static_assert(8 % WM == 0 && 8 % WN == 0, "load split");
 };
 
@@ -237,9 +239,18 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
     }
 }
 
-template <int WN, int WM, bool MOE>
+// PING: the two wave groups (rows wm = 0 and wm = 1 of the wave grid; waves w
+// and w + 4 share a SIMD) run half a K step apart.  Per K step there are two
+// barriers; between them one group issues its MFMAs while the other converts
+// and rescales its previous block (VALU), so each SIMD keeps its matrix core
+// and its vector ALU busy at the same time.
+template <int WN, int WM, bool MOE, bool PING>
 __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    // (device pass only: the body's address-space casts are not valid host
+    // code, and the host pass only needs the launch stub)
     using C = TileCfg<WN, WM>;
+    static_assert(!PING || (WM == 2 && WN == 4), "ping-pong pairs waves w and w + 4 on one SIMD");
     __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds2[C::kStageBytes];
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     if (t.rows <= 0) return;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t K = p.K, KB = p.KB;
 
     // Each range covers only this tile's rows (<= 2^31 bytes since K <= 2^23),
@@ -258,6 +269,10 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * KB, clamp_bytes(t.rows * KB * 4));
+
+    // Activation scale of tile row r sits in wave (r / kScaleRowsPerWave)'s
+    // slot, lane r % kScaleRowsPerWave.
+    auto srow_off = [](int r) { return C::kSOff + 256 * (r / C::kScaleRowsPerWave) + 4 * (r % C::kScaleRowsPerWave); };
 
     // Per-lane load descriptors.  Load piece q (1 KB) covers tile rows
     // [8q, 8q+8); lane i lands at LDS row 8q + i/8, 16-byte slot i%8, which
@@ -269,45 +284,44 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     for (int j = 0; j < C::kWLoads; ++j) {
         const int q = wave + j * C::kWaves;
         const int c = (lane & 7) ^ r_in ^ (q & 1);
-        wchunk[j] = c;
+        wchunk[j] = 16 * c;
         wgo[j] = (uint32_t)((8 * q + r_in) * K + 16 * c);
     }
 #pragma unroll
     for (int j = 0; j < C::kXLoads; ++j) {
         const int q = wave + j * C::kWaves;
         const int c = (lane & 7) ^ r_in ^ (q & 1);
-        xchunk[j] = c;
+        xchunk[j] = 16 * c;
         xgo[j] = (uint32_t)((8 * q + r_in) * K + 16 * c);
     }
-    const bool loads_scales = wave < WM;
+    const uint32_t sgo = (uint32_t)((C::kScaleRowsPerWave * wave + lane) * KB * 4);
 
     // Issue one stage's buffer->LDS loads for K block kb.  A chunk at or past
-    // K (the K tail, and every chunk of a block kb >= KB) reads as zero.  The
-    // scale piece of a block kb >= KB is clamped to the last block: that stage
+    // K (the K tail, and every chunk of a block kb >= KB) reads as zero; the
+    // check is a per-lane select with no branch (a branch here makes the
+    // compiler lose track of which stage each LDS fill writes and drain the
+    // prefetch).  Every wave also fills kBM / kWaves rows of the activation
+    // scales (one lane per row), so all waves issue the same number of loads.
+    // The scale of a block kb >= KB is clamped to the last block: that stage
     // is never consumed.
-    auto issue = [&](char *stage, int64_t kb) {
+    auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
         const int64_t k0 = kb * kBlock;
         const uint32_t kofs = (uint32_t)k0;
 #pragma unroll
-        for (int j = 0; j < C::kWLoads; ++j) {
-            const int q = wave + j * C::kWaves;
-            const uint32_t off = (k0 + 16 * wchunk[j] < K) ? wgo[j] + kofs : kOobOffset;
+        for (int j = 0; j < C::kWLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (BI8_LDS void *)(stage + C::kWOff + q * 1024), 16, off, 0, 0, 0);
-        }
+                wr, (BI8_LDS void *)(stage + C::kWOff + (wave + j * C::kWaves) * 1024), 16,
+                (k0 + wchunk[j] < K) ? wgo[j] + kofs : kOobOffset, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < C::kXLoads; ++j) {
-            const int q = wave + j * C::kWaves;
-            const uint32_t off = (k0 + 16 * xchunk[j] < K) ? xgo[j] + kofs : kOobOffset;
+        for (int j = 0; j < C::kXLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (BI8_LDS void *)(stage + C::kXOff + q * 1024), 16, off, 0, 0, 0);
-        }
-        if (loads_scales) {
-            const int64_t r = 64 * wave + lane;
+                xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
+                (k0 + xchunk[j] < K) ? xgo[j] + kofs : kOobOffset, 0, 0, 0);
+        {
             const int64_t kbc = kb < KB ? kb : KB - 1;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 sr, (BI8_LDS void *)(stage + C::kSOff + 256 * wave), 4,
-                (uint32_t)((r * KB + kbc) * 4), 0, 0, 0);
+                lane < C::kScaleRowsPerWave ? sgo + (uint32_t)(kbc * 4) : kOobOffset, 0, 0, 0);
         }
     };
 
@@ -321,11 +335,15 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
     const int wrow0 = C::kWOff + (wn * 64 + rr) * 128;
     const int xrow0 = C::kXOff + (wm * 64 + rr) * 128;
-    const int srow0 = C::kSOff + (wm * 64 + rr) * 4;
+    const int srow0 = srow_off(wm * 64 + rr), srow1 = srow_off(wm * 64 + 32 + rr);
 
     int64_t nbw = (t.n0 + wn * 64) / kBlock;
     if (nbw > p.NB - 1) nbw = p.NB - 1;
-    const float *ws_row = t.ws + nbw * KB;
+    // The wave's weight-scale row, read through the constant address space so
+    // that the wave-uniform loads become scalar loads (the scales are never
+    // written while the kernel runs).
+    const BI8_CONST float *ws_row = reinterpret_cast<const BI8_CONST float *>(
+        reinterpret_cast<uintptr_t>(t.ws + nbw * KB));
 
     i32x16 zero16;
 #pragma unroll
@@ -338,63 +356,85 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) y[a][b][i] = 0.f;
 
-    auto compute = [&](const char *stage, int64_t kb) {
+    // MFMA phase: the block's int32 sums for the wave's 2 x 2 sub-tiles, plus
+    // the scales the rescale will need (read now: the stage may be refilled
+    // before the rescale runs).
+    i32x16 acc[2][2];
+    float xsv[2], wsv = 0.f;
+    auto mma = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
         i32x4 wf[2][4], xf[2][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                wf[a][s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
+        }
+        xsv[0] = *reinterpret_cast<const float *>(stage + srow0);
+        xsv[1] = *reinterpret_cast<const float *>(stage + srow1);
+        wsv = ws_row[kb];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        wf[a][s], xf[b][s], s == 0 ? zero16 : acc[a][b], 0, 0, 0);
+        // the MFMAs belong to this phase
+        asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+    };
+    // Rescale phase: y += float(acc) * (xs * ws) per sub-tile.
+    auto epi = [&]() __attribute__((always_inline)) {
+        const float tb[2] = {xsv[0] * wsv, xsv[1] * wsv};
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                wf[a][s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
-        const float xs0 = *reinterpret_cast<const float *>(stage + srow0);
-        const float xs1 = *reinterpret_cast<const float *>(stage + srow0 + 32 * 4);
-        const float wsv = ws_row[kb];
-        const float tb[2] = {xs0 * wsv, xs1 * wsv};
-        // Sub-tile by sub-tile: a chain of 4 accumulating MFMAs over the block,
-        // then its rescale, which can overlap the next sub-tile's chain.
-#pragma unroll
-        for (int ab = 0; ab < 4; ++ab) {
-            const int a = ab >> 1, b = ab & 1;
-            i32x16 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a][0], xf[b][0], zero16, 0, 0, 0);
-#pragma unroll
-            for (int s = 1; s < 4; ++s)
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a][s], xf[b][s], acc, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) y[a][b][i] = fmaf((float)acc[i], tb[b], y[a][b][i]);
-        }
-        // The rescale of this block must finish inside its step: without this
-        // the optimiser sinks it into later steps and keeps several blocks'
-        // int32 accumulators alive.
+                for (int i = 0; i < 16; ++i)
+                    y[a][b][i] = fmaf((float)acc[a][b][i], tb[b], y[a][b][i]);
+        // the rescale belongs to this phase
         asm volatile("" : "+v"(y[0][0]), "+v"(y[0][1]), "+v"(y[1][0]), "+v"(y[1][1]));
     };
+    auto wait_stage = [&]() __attribute__((always_inline)) { wait_vmcnt<C::kLoads>(); };
 
-    // 3-stage ring: stage kb lives in lds[kb % 3]; loads run two steps ahead.
-    auto step = [&](char *cur, char *ahead, int64_t kb) {
-        if (loads_scales)
-            wait_vmcnt<C::kTileLoads + 1>();
-        else
-            wait_vmcnt<C::kTileLoads>();
+    // 3-stage ring: block kb lives in lds[kb % 3]; loads run two blocks ahead.
+    // Before the first barrier of step kb, this wave's loads of block kb are
+    // complete (only block kb + 1's are still in flight).
+    auto step = [&](const int group, char *cur, char *ahead, int64_t kb) __attribute__((always_inline)) {
+        wait_stage();
         lds_barrier();
         issue(ahead, kb + 2);
-        compute(cur, kb);
-        // keep each block's MFMAs and rescale inside its own step (bounds the
-        // live accumulators)
-        __builtin_amdgcn_sched_barrier(0);
+        if (!PING || group == 0) {
+            mma(cur, kb);
+            if (PING) lds_barrier();
+            epi();
+        } else {
+            if (kb > 0) epi();   // block kb - 1
+            lds_barrier();
+            mma(cur, kb);
+        }
     };
-    issue(lds0, 0);
-    issue(lds1, 1);
-    int64_t kb = 0;
-    for (; kb + 3 <= KB; kb += 3) {
-        step(lds0, lds2, kb);
-        step(lds1, lds0, kb + 1);
-        step(lds2, lds1, kb + 2);
-    }
-    if (kb < KB) step(lds0, lds2, kb++);
-    if (kb < KB) step(lds1, lds0, kb++);
+    auto run = [&](const int group) __attribute__((always_inline)) {
+        issue(lds0, 0);
+        issue(lds1, 1);
+        int64_t kb = 0;
+        for (; kb + 3 <= KB; kb += 3) {
+            step(group, lds0, lds2, kb);
+            step(group, lds1, lds0, kb + 1);
+            step(group, lds2, lds1, kb + 2);
+        }
+        if (kb < KB) step(group, lds0, lds2, kb++);
+        if (kb < KB) step(group, lds1, lds0, kb++);
+        if (PING && group == 1) epi();   // the last block
+    };
+    if (!PING || wm == 0)
+        run(0);
+    else
+        run(1);
     wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
 
     // Store.  32x32 result layout: lane -> token column (lane & 31); element i
@@ -429,15 +469,22 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
             }
         }
     }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int WN, int WM, bool MOE>
+// Explicit instantiations: the host pass must emit a launch stub for every
+// variant launched below.
+template __global__ void gemm_tiled_kernel<4, 2, false, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, true, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<2, 1, false, false>(GemmArgs);
+
+template <int WN, int WM, bool MOE, bool PING>
 hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
     using C = TileCfg<WN, WM>;
     const int64_t total = p.tiles_m * p.tiles_n;
     if (total <= 0) return hipSuccess;
     if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, MOE>), dim3((unsigned)total), dim3(C::kThreads),
+    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, MOE, PING>), dim3((unsigned)total), dim3(C::kThreads),
                        0, stream, p);
     return hipGetLastError();
 }
@@ -492,11 +539,11 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
         case GemmPath::kTiledLarge:
             p.tiles_m = (M + 127) / 128;
             p.tiles_n = (N + 255) / 256;
-            return launch_tiled<4, 2, false>(p, stream);
+            return launch_tiled<4, 2, false, true>(p, stream);
         case GemmPath::kTiledSmall:
             p.tiles_m = (M + 63) / 64;
             p.tiles_n = (N + 127) / 128;
-            return launch_tiled<2, 1, false>(p, stream);
+            return launch_tiled<2, 1, false, false>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -509,7 +556,7 @@ hipError_t launch_moe_gemm(const int8_t *xq, const float *xs, const int32_t *off
     p.E = E;
     p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
     p.tiles_n = (N + 255) / 256;
-    return launch_tiled<4, 2, true>(p, stream);
+    return launch_tiled<4, 2, true, true>(p, stream);
 }
 
 }  // namespace bi8
