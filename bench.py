@@ -275,7 +275,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--copies", type=int, default=None,
                     help="weight copies to rotate over (default: enough to exceed the Infinity Cache)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (x16 launches), for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters to bytes, and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.randint(0, 127, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(16):
+            torch.add(src, 1, out=dst)   # one elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 16}), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
