@@ -171,14 +171,17 @@ struct TileCfg {
     static constexpr int kBM = 64 * WM;              // activation rows per tile
     static constexpr int kWOff = 0;                  // LDS layout of one stage
     static constexpr int kXOff = kBN * 128;
-    static constexpr int kSOff = kXOff + kBM * 128;
-    static constexpr int kStageBytes = kSOff + kWaves * 256;   // one 256 B scale slot per wave
+    static constexpr int kStageBytes = kXOff + kBM * 128;
     static constexpr int kWLoads = 8 / WM;           // 1 KB W pieces per wave per stage
     static constexpr int kXLoads = 8 / WN;           // 1 KB X pieces per wave per stage
     static constexpr int kTileLoads = kWLoads + kXLoads;
-    static constexpr int kScaleRowsPerWave = kBM / kWaves;   // one activation-scale DMA per wave
-    static constexpr int kLoads = kTileLoads + 1;            // loads per wave per stage
+    // Activation scales travel in batches of kSB K blocks: one 32-byte run per
+    // tile row and batch (one memory line) instead of one 4-byte gather per
+    // row and block.  kScaleLoads dword loads per wave carry one batch.
+    static constexpr int kSB = 8;
+    static constexpr int kScaleLoads = kBM * kSB / 64 / kWaves;
     static_assert(8 % WM == 0 && 8 % WN == 0, "load split");
+    static_assert(kScaleLoads >= 1 && kBM * kSB % (64 * kWaves) == 0, "scale batch split");
 };
 
 // Spread consecutive workgroup ids (dispatched round-robin over the 8 XCDs)
@@ -254,6 +257,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds2[C::kStageBytes];
+    __shared__ float xsl[2][C::kBM * C::kSB];   // activation-scale batches, double-buffered
 
     Tile t;
     if (!decode_tile<C::kBN, C::kBM, MOE>(p, t)) return;
@@ -269,10 +273,6 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * KB, clamp_bytes(t.rows * KB * 4));
-
-    // Activation scale of tile row r sits in wave (r / kScaleRowsPerWave)'s
-    // slot, lane r % kScaleRowsPerWave.
-    auto srow_off = [](int r) { return C::kSOff + 256 * (r / C::kScaleRowsPerWave) + 4 * (r % C::kScaleRowsPerWave); };
 
     // Per-lane load descriptors.  Load piece q (1 KB) covers tile rows
     // [8q, 8q+8); lane i lands at LDS row 8q + i/8, 16-byte slot i%8, which
@@ -294,19 +294,28 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
         xchunk[j] = 16 * c;
         xgo[j] = (uint32_t)((8 * q + r_in) * K + 16 * c);
     }
-    const uint32_t sgo = (uint32_t)((C::kScaleRowsPerWave * wave + lane) * KB * 4);
+    // Scale batch layout (per buffer): row-major [kBM rows][kSB blocks]; this
+    // wave's load j covers flat entries f = (wave * kScaleLoads + j) * 64 + lane.
+    float sv[C::kScaleLoads];
 
     // Issue one stage's buffer->LDS loads for K block kb.  A chunk at or past
     // K (the K tail, and every chunk of a block kb >= KB) reads as zero; the
     // check is a per-lane select with no branch (a branch here makes the
     // compiler lose track of which stage each LDS fill writes and drain the
-    // prefetch).  Every wave also fills kBM / kWaves rows of the activation
-    // scales (one lane per row), so all waves issue the same number of loads.
-    // The scale of a block kb >= KB is clamped to the last block: that stage
-    // is never consumed.
+    // prefetch).  With the first block of a scale batch, the batch's scales
+    // are loaded into registers (issued first, so they complete with the
+    // stage); they are written to LDS one step before the batch is used.
     auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
         const int64_t k0 = kb * kBlock;
         const uint32_t kofs = (uint32_t)k0;
+        if ((kb & (C::kSB - 1)) == 0) {
+#pragma unroll
+            for (int j = 0; j < C::kScaleLoads; ++j) {
+                const int f = (wave * C::kScaleLoads + j) * 64 + lane;
+                const int64_t g = kb + (f & (C::kSB - 1));
+                sv[j] = buf_load_f32(sr, g < KB ? (uint32_t)(((f / C::kSB) * KB + g) * 4) : kOobOffset);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -317,12 +326,14 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
                 (k0 + xchunk[j] < K) ? xgo[j] + kofs : kOobOffset, 0, 0, 0);
-        {
-            const int64_t kbc = kb < KB ? kb : KB - 1;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                sr, (BI8_LDS void *)(stage + C::kSOff + 256 * wave), 4,
-                lane < C::kScaleRowsPerWave ? sgo + (uint32_t)(kbc * 4) : kOobOffset, 0, 0, 0);
-        }
+    };
+    // Write the scale batch held in registers to LDS buffer `half`, and make it
+    // visible before the next barrier.
+    auto store_scales = [&](const int64_t half) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < C::kScaleLoads; ++j)
+            xsl[half][(wave * C::kScaleLoads + j) * 64 + lane] = sv[j];
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // lgkmcnt(0)
     };
 
     // Fragment read addresses (32x32x32 operand layout: lane -> row lane & 31,
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
     const int wrow0 = C::kWOff + (wn * 64 + rr) * 128;
     const int xrow0 = C::kXOff + (wm * 64 + rr) * 128;
-    const int srow0 = srow_off(wm * 64 + rr), srow1 = srow_off(wm * 64 + 32 + rr);
+    const int srow0 = (wm * 64 + rr) * C::kSB, srow1 = (wm * 64 + 32 + rr) * C::kSB;
 
     int64_t nbw = (t.n0 + wn * 64) / kBlock;
     if (nbw > p.NB - 1) nbw = p.NB - 1;
@@ -372,8 +383,8 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
             for (int b = 0; b < 2; ++b)
                 xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
         }
-        xsv[0] = *reinterpret_cast<const float *>(stage + srow0);
-        xsv[1] = *reinterpret_cast<const float *>(stage + srow1);
+        xsv[0] = xsl[(kb / C::kSB) & 1][srow0 + (kb & (C::kSB - 1))];
+        xsv[1] = xsl[(kb / C::kSB) & 1][srow1 + (kb & (C::kSB - 1))];
         wsv = ws_row[kb];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -399,13 +410,20 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
         // the rescale belongs to this phase
         asm volatile("" : "+v"(y[0][0]), "+v"(y[0][1]), "+v"(y[1][0]), "+v"(y[1][1]));
     };
-    auto wait_stage = [&]() __attribute__((always_inline)) { wait_vmcnt<C::kLoads>(); };
+    // Before step kb, only block kb + 1's loads may still be in flight (plus
+    // its scale batch when block kb + 1 starts one).
+    auto wait_stage = [&](int64_t kb) __attribute__((always_inline)) {
+        if (((kb + 1) & (C::kSB - 1)) == 0)
+            wait_vmcnt<C::kTileLoads + C::kScaleLoads>();
+        else
+            wait_vmcnt<C::kTileLoads>();
+    };
 
     // 3-stage ring: block kb lives in lds[kb % 3]; loads run two blocks ahead.
     // Before the first barrier of step kb, this wave's loads of block kb are
     // complete (only block kb + 1's are still in flight).
     auto step = [&](const int group, char *cur, char *ahead, int64_t kb) __attribute__((always_inline)) {
-        wait_stage();
+        wait_stage(kb);
         lds_barrier();
         issue(ahead, kb + 2);
         if (!PING || group == 0) {
@@ -417,10 +435,14 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
             lds_barrier();
             mma(cur, kb);
         }
+        // the next block opens a new scale batch: publish it (its loads were
+        // issued with block kb + 1's stage, a step ago)
+        if (((kb + 1) & (C::kSB - 1)) == 0) store_scales(((kb + 1) / C::kSB) & 1);
     };
     auto run = [&](const int group) __attribute__((always_inline)) {
         issue(lds0, 0);
         issue(lds1, 1);
+        store_scales(0);
         int64_t kb = 0;
         for (; kb + 3 <= KB; kb += 3) {
             step(group, lds0, lds2, kb);
