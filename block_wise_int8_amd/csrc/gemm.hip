@@ -124,6 +124,10 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
             }
             wsv[u] = ws_row[ok ? b : KB - 1];
         }
+        // every load above is issued before the first MFMA: without this the
+        // scheduler interleaves loads and MFMAs and the wave pays several HBM
+        // round trips instead of one
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kSkinnyUnroll; ++u) {
 #pragma unroll
@@ -163,24 +167,30 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
 // Tiled path
 // ---------------------------------------------------------------------------
 
-template <int WN, int WM>
+// WN x WM waves per workgroup; each wave owns SA x SB sub-tiles of 32 x 32
+// (weight rows x activation rows).
+template <int WN, int WM, int SA, int SB>
 struct TileCfg {
     static constexpr int kWaves = WN * WM;
     static constexpr int kThreads = kWaves * 64;
-    static constexpr int kBN = 64 * WN;              // weight rows per tile
-    static constexpr int kBM = 64 * WM;              // activation rows per tile
+    static constexpr int kWaveN = 32 * SA;           // weight rows per wave
+    static constexpr int kWaveM = 32 * SB;           // activation rows per wave
+    static constexpr int kBN = kWaveN * WN;          // weight rows per tile
+    static constexpr int kBM = kWaveM * WM;          // activation rows per tile
     static constexpr int kWOff = 0;                  // LDS layout of one stage
     static constexpr int kXOff = kBN * 128;
     static constexpr int kStageBytes = kXOff + kBM * 128;
-    static constexpr int kWLoads = 8 / WM;           // 1 KB W pieces per wave per stage
-    static constexpr int kXLoads = 8 / WN;           // 1 KB X pieces per wave per stage
+    static constexpr int kWLoads = kBN / 8 / kWaves; // 1 KB W pieces per wave per stage
+    static constexpr int kXLoads = kBM / 8 / kWaves; // 1 KB X pieces per wave per stage
     static constexpr int kTileLoads = kWLoads + kXLoads;
     // Activation scales travel in batches of kSB K blocks: one 32-byte run per
     // tile row and batch (one memory line) instead of one 4-byte gather per
     // row and block.  kScaleLoads dword loads per wave carry one batch.
     static constexpr int kSB = 8;
     static constexpr int kScaleLoads = kBM * kSB / 64 / kWaves;
-    static_assert(8 % WM == 0 && 8 % WN == 0, "load split");
+    static_assert(kWLoads >= 1 && kXLoads >= 1 && kBN % (8 * kWaves) == 0 && kBM % (8 * kWaves) == 0,
+                  "load split");
+    static_assert(128 % kWaveN == 0, "a wave's weight rows lie in one 128-row scale block");
     static_assert(kScaleLoads >= 1 && kBM * kSB % (64 * kWaves) == 0, "scale batch split");
 };
 
@@ -247,12 +257,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
 // barriers; between them one group issues its MFMAs while the other converts
 // and rescales its previous block (VALU), so each SIMD keeps its matrix core
 // and its vector ALU busy at the same time.
-template <int WN, int WM, bool MOE, bool PING>
+template <int WN, int WM, int SA, int SB, bool MOE, bool PING>
 __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     // (device pass only: the body's address-space casts are not valid host
     // code, and the host pass only needs the launch stub)
-    using C = TileCfg<WN, WM>;
+    using C = TileCfg<WN, WM, SA, SB>;
     static_assert(!PING || (WM == 2 && WN == 4), "ping-pong pairs waves w and w + 4 on one SIMD");
     __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
@@ -344,11 +354,13 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     int frag_off[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
-    const int wrow0 = C::kWOff + (wn * 64 + rr) * 128;
-    const int xrow0 = C::kXOff + (wm * 64 + rr) * 128;
-    const int srow0 = (wm * 64 + rr) * C::kSB, srow1 = (wm * 64 + 32 + rr) * C::kSB;
+    const int wrow0 = C::kWOff + (wn * C::kWaveN + rr) * 128;
+    const int xrow0 = C::kXOff + (wm * C::kWaveM + rr) * 128;
+    int srow[SB];
+#pragma unroll
+    for (int b = 0; b < SB; ++b) srow[b] = (wm * C::kWaveM + 32 * b + rr) * C::kSB;
 
-    int64_t nbw = (t.n0 + wn * 64) / kBlock;
+    int64_t nbw = (t.n0 + wn * C::kWaveN) / kBlock;
     if (nbw > p.NB - 1) nbw = p.NB - 1;
     // The wave's weight-scale row, read through the constant address space so
     // that the wave-uniform loads become scalar loads (the scales are never
@@ -359,56 +371,65 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     i32x16 zero16;
 #pragma unroll
     for (int i = 0; i < 16; ++i) zero16[i] = 0;
-    f32x16 y[2][2];
+    f32x16 y[SA][SB];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < SA; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < SB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) y[a][b][i] = 0.f;
 
     // MFMA phase: the block's int32 sums for the wave's 2 x 2 sub-tiles, plus
     // the scales the rescale will need (read now: the stage may be refilled
     // before the rescale runs).
-    i32x16 acc[2][2];
-    float xsv[2], wsv = 0.f;
+    i32x16 acc[SA][SB];
+    float xsv[SB], wsv = 0.f;
     auto mma = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
-        i32x4 wf[2][4], xf[2][4];
+        i32x4 wf[SA][4], xf[SB][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < SA; ++a)
                 wf[a][s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < SB; ++b)
                 xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
         }
-        xsv[0] = xsl[(kb / C::kSB) & 1][srow0 + (kb & (C::kSB - 1))];
-        xsv[1] = xsl[(kb / C::kSB) & 1][srow1 + (kb & (C::kSB - 1))];
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+            xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
         wsv = ws_row[kb];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < SA; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < SB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                         wf[a][s], xf[b][s], s == 0 ? zero16 : acc[a][b], 0, 0, 0);
         // the MFMAs belong to this phase
-        asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+#pragma unroll
+        for (int a = 0; a < SA; ++a)
+#pragma unroll
+            for (int b = 0; b < SB; ++b) asm volatile("" : "+v"(acc[a][b]));
     };
     // Rescale phase: y += float(acc) * (xs * ws) per sub-tile.
     auto epi = [&]() __attribute__((always_inline)) {
-        const float tb[2] = {xsv[0] * wsv, xsv[1] * wsv};
+        float tb[SB];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < SB; ++b) tb[b] = xsv[b] * wsv;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+        for (int a = 0; a < SA; ++a)
+#pragma unroll
+            for (int b = 0; b < SB; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     y[a][b][i] = fmaf((float)acc[a][b][i], tb[b], y[a][b][i]);
         // the rescale belongs to this phase
-        asm volatile("" : "+v"(y[0][0]), "+v"(y[0][1]), "+v"(y[1][0]), "+v"(y[1][1]));
+#pragma unroll
+        for (int a = 0; a < SA; ++a)
+#pragma unroll
+            for (int b = 0; b < SB; ++b) asm volatile("" : "+v"(y[a][b]));
     };
     // Before step kb, only block kb + 1's loads may still be in flight (plus
     // its scale batch when block kb + 1 starts one).
@@ -462,15 +483,15 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     // Store.  32x32 result layout: lane -> token column (lane & 31); element i
     // -> weight row 8 * (i / 4) + 4 * (lane >> 5) + (i % 4).
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int64_t ml = wm * 64 + b * 32 + rr;
+    for (int b = 0; b < SB; ++b) {
+        const int64_t ml = wm * C::kWaveM + b * 32 + rr;
         if (ml >= t.rows) continue;
         uint16_t *yrow = p.y + (t.m0 + ml) * p.N;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < SA; ++a) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const int64_t n = t.n0 + wn * 64 + a * 32 + 8 * i4 + 4 * hi;
+                const int64_t n = t.n0 + wn * C::kWaveN + a * 32 + 8 * i4 + 4 * hi;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -496,17 +517,17 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 
 // Explicit instantiations: the host pass must emit a launch stub for every
 // variant launched below.
-template __global__ void gemm_tiled_kernel<4, 2, false, true>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, true, true>(GemmArgs);
-template __global__ void gemm_tiled_kernel<2, 1, false, false>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true>(GemmArgs);
 
-template <int WN, int WM, bool MOE, bool PING>
+template <int WN, int WM, int SA, int SB, bool MOE, bool PING>
 hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
-    using C = TileCfg<WN, WM>;
+    using C = TileCfg<WN, WM, SA, SB>;
     const int64_t total = p.tiles_m * p.tiles_n;
     if (total <= 0) return hipSuccess;
     if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, MOE, PING>), dim3((unsigned)total), dim3(C::kThreads),
+    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, SA, SB, MOE, PING>), dim3((unsigned)total), dim3(C::kThreads),
                        0, stream, p);
     return hipGetLastError();
 }
@@ -561,11 +582,11 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
         case GemmPath::kTiledLarge:
             p.tiles_m = (M + 127) / 128;
             p.tiles_n = (N + 255) / 256;
-            return launch_tiled<4, 2, false, true>(p, stream);
+            return launch_tiled<4, 2, 2, 2, false, true>(p, stream);
         case GemmPath::kTiledSmall:
             p.tiles_m = (M + 63) / 64;
             p.tiles_n = (N + 127) / 128;
-            return launch_tiled<2, 1, false, false>(p, stream);
+            return launch_tiled<4, 2, 1, 1, false, true>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -578,7 +599,7 @@ hipError_t launch_moe_gemm(const int8_t *xq, const float *xs, const int32_t *off
     p.E = E;
     p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
     p.tiles_n = (N + 255) / 256;
-    return launch_tiled<4, 2, true, true>(p, stream);
+    return launch_tiled<4, 2, 2, 2, true, true>(p, stream);
 }
 
 }  // namespace bi8
