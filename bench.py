@@ -39,6 +39,9 @@ import workloads as wl  # noqa: E402
 
 METRIC = "block-int8 GEMM TOPS + fraction of int8 MFMA/HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+VARIANTS = {"auto": None, "skinny": bi8.GEMM_SKINNY, "128x64": bi8.GEMM_TILE_128X64,
+            "256x128": bi8.GEMM_TILE_256X128, "256x256": bi8.GEMM_TILE_256X256}
+VARIANT_NAMES = {v: k for k, v in VARIANTS.items() if v is not None}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
 ROTATE_BYTES = 540 << 20       # > Infinity Cache (256 MB)
 MAX_COPIES = 64
@@ -75,9 +78,10 @@ def n_copies(weight_bytes, override=None):
 class Dense:
     """quant_act + gemm on one [M, K] x [N, K] linear."""
 
-    def __init__(self, name, copies=None):
+    def __init__(self, name, copies=None, variant=None):
         c = wl.CONFIGS[name]
         self.name = name
+        self.variant = variant
         self.M, self.N, self.K = c["M"], c["N"], c["K"]
         rng = wl.rng_for(c["seed"])
         self.x_np = wl.activations(rng, self.M, self.K, c.get("outlier_frac", 0.0))
@@ -106,15 +110,16 @@ class Dense:
 
     def dominant_launch(self, i):
         j = i % self.copies
-        bi8.gemm(self.xq, self.xs, self.w[j], self.ws[j], y=self.y)
+        bi8.gemm(self.xq, self.xs, self.w[j], self.ws[j], y=self.y, variant=self.variant)
 
     def step(self, i):
         self.quant(i)
         self.dominant_launch(i)
 
     def config(self):
+        v = bi8.gemm_select(self.M, self.N, self.K) if self.variant is None else self.variant
         return {"workload": self.workload, "M": self.M, "K": self.K, "N": self.N,
-                "block": [128, 128], "weight_copies": self.copies}
+                "block": [128, 128], "weight_copies": self.copies, "kernel": VARIANT_NAMES[v]}
 
     def cpu_sample(self, budget_s):
         """Time the oracle (quant + GEMM) on a bounded sample of rows."""
@@ -139,9 +144,10 @@ class Dense:
 class Moe:
     """quant_act + grouped gemm for w13, then quant_act + grouped gemm for w2."""
 
-    def __init__(self):
+    def __init__(self, variant=None):
         c = wl.CONFIGS["moe"]
         self.name = "moe"
+        self.variant = variant
         T, H, I, E, k = c["T"], c["H"], c["I"], c["E"], c["topk"]
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         rng = wl.rng_for(c["seed"])
@@ -181,17 +187,20 @@ class Moe:
         bi8.quant_act(self.x, self.xq1, self.xs1)
 
     def dominant_launch(self, i):
-        bi8.moe_gemm(self.xq1, self.xs1, self.off, self.w13, self.ws13, y=self.y13)
+        bi8.moe_gemm(self.xq1, self.xs1, self.off, self.w13, self.ws13, y=self.y13, variant=self.variant)
 
     def step(self, i):
         self.quant(i)
         self.dominant_launch(i)
         bi8.quant_act(self.x2, self.xq2, self.xs2)
-        bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2)
+        bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2, variant=self.variant)
 
     def config(self):
+        v = (bi8.moe_gemm_select(self.R, 2 * self.I, self.H, self.E) if self.variant is None
+             else self.variant)
         return {"workload": self.workload, "T": self.T, "E": self.E, "topk": self.k,
-                "hidden": self.H, "intermediate": self.I, "rows": self.R, "block": [128, 128]}
+                "hidden": self.H, "intermediate": self.I, "rows": self.R, "block": [128, 128],
+                "kernel": VARIANT_NAMES[v]}
 
     def cpu_sample(self, budget_s):
         import oracle
@@ -210,8 +219,8 @@ class Moe:
         return ops / dt / 1e12, "%d rows of expert 0, w13 projection, quant+GEMM, %.1f s" % (rows, dt)
 
 
-def make_workload(name, copies=None):
-    return Moe() if name == "moe" else Dense(name, copies)
+def make_workload(name, copies=None, variant=None):
+    return Moe(variant) if name == "moe" else Dense(name, copies, variant)
 
 
 def capture(fn, steps):
@@ -273,6 +282,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS),
+                    help="GEMM kernel (default: the library's shape-based choice)")
     ap.add_argument("--copies", type=int, default=None,
                     help="weight copies to rotate over (default: enough to exceed the Infinity Cache)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -301,7 +312,7 @@ def main():
 
     bi8.load()
     log("[bench] setting up workload %s" % args.workload)
-    w = make_workload(args.workload, args.copies)
+    w = make_workload(args.workload, args.copies, VARIANTS[args.variant])
     use_graph = not args.eager
 
     log("[bench] warmup %d steps" % args.warmup)

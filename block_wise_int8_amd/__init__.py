@@ -12,6 +12,9 @@ Entry points (same names as the C ABI, without the ``blockint8_`` prefix):
 * :func:`gemm`       -- y = bf16(block-scaled int8 GEMM (+ bias)), [M, N]
 * :func:`moe_gemm`   -- the same per expert over expert-sorted rows
 * :func:`linear`     -- quant_act followed by gemm (the dynamic-scale linear)
+
+``gemm`` and ``moe_gemm`` pick a kernel by shape (:func:`gemm_select`,
+:func:`moe_gemm_select`); their ``variant`` argument names one instead.
 """
 from __future__ import annotations
 
@@ -21,9 +24,12 @@ import os
 import torch
 
 __all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "moe_gemm",
-           "linear", "BLOCK"]
+           "linear", "gemm_select", "moe_gemm_select", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
+           "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
 
 BLOCK = 128
+# kernel variant ids (BI8_GEMM_* in the C header)
+GEMM_AUTO, GEMM_SKINNY, GEMM_TILE_128X64, GEMM_TILE_256X128, GEMM_TILE_256X256 = range(5)
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libblockint8.so"
 _lib = None
@@ -63,7 +69,12 @@ def load() -> ctypes.CDLL:
     lib.blockint8_quant_act.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp]
     lib.blockint8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     lib.blockint8_moe_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
-    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm"):
+    lib.blockint8_gemm_select.argtypes = [i64, i64, i64]
+    lib.blockint8_moe_gemm_select.argtypes = [i64, i64, i64, i32]
+    lib.blockint8_gemm_variant.argtypes = [i32] + lib.blockint8_gemm.argtypes
+    lib.blockint8_moe_gemm_variant.argtypes = [i32] + lib.blockint8_moe_gemm.argtypes
+    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_gemm_select",
+              "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -130,10 +141,23 @@ def quant_act(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tensor 
     return xq, xs
 
 
+def gemm_select(M: int, N: int, K: int) -> int:
+    """The kernel variant (``GEMM_*``) that ``gemm`` runs for this shape."""
+    return int(load().blockint8_gemm_select(M, N, K))
+
+
+def moe_gemm_select(R: int, N: int, K: int, E: int) -> int:
+    """The kernel variant (``GEMM_*``) that ``moe_gemm`` runs for this shape."""
+    return int(load().blockint8_moe_gemm_select(R, N, K, E))
+
+
 def gemm(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tensor,
          bias: torch.Tensor | None = None, y: torch.Tensor | None = None,
-         block=(BLOCK, BLOCK)) -> torch.Tensor:
-    """Block-scaled int8 GEMM ``y = x . W^T`` -> bf16 [M, N]."""
+         block=(BLOCK, BLOCK), variant: int | None = None) -> torch.Tensor:
+    """Block-scaled int8 GEMM ``y = x . W^T`` -> bf16 [M, N].
+
+    ``variant`` (one of ``GEMM_*``) runs a named kernel instead of the
+    shape-based choice."""
     _need(xq, "xq", torch.int8, 2)
     _need(xs, "xs", torch.float32, 2)
     _need(w, "w", torch.int8, 2)
@@ -154,17 +178,23 @@ def gemm(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tensor,
     _need(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    _check(load().blockint8_gemm(_ptr(xq), _ptr(xs), _ptr(w), _ptr(ws), _ptr(bias), _ptr(y),
-                                 M, N, K, block[0], block[1], _stream_handle(xq.device)))
+    args = (_ptr(xq), _ptr(xs), _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K, block[0], block[1],
+            _stream_handle(xq.device))
+    if variant is None:
+        _check(load().blockint8_gemm(*args))
+    else:
+        _check(load().blockint8_gemm_variant(int(variant), *args))
     return y
 
 
 def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w: torch.Tensor,
-             ws: torch.Tensor, y: torch.Tensor | None = None, block=(BLOCK, BLOCK)) -> torch.Tensor:
+             ws: torch.Tensor, y: torch.Tensor | None = None, block=(BLOCK, BLOCK),
+             variant: int | None = None) -> torch.Tensor:
     """Grouped block-scaled int8 GEMM over expert-sorted rows -> bf16 [R, N].
 
     ``expert_offsets`` is int32 [E+1] on the device (rows [off[e], off[e+1])
     use expert e); ``w`` is int8 [E, N, K], ``ws`` fp32 [E, ceil(N/128), ceil(K/128)].
+    ``variant`` runs a named kernel (``GEMM_TILE_256X128`` or ``GEMM_TILE_256X256``).
     """
     _need(xq, "xq", torch.int8, 2)
     _need(xs, "xs", torch.float32, 2)
@@ -185,9 +215,12 @@ def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w
     _need(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (R, N):
         raise ValueError("y must be [R, N]")
-    _check(load().blockint8_moe_gemm(_ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(w), _ptr(ws),
-                                     _ptr(y), R, N, K, E, block[0], block[1],
-                                     _stream_handle(xq.device)))
+    args = (_ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(w), _ptr(ws), _ptr(y), R, N, K, E,
+            block[0], block[1], _stream_handle(xq.device))
+    if variant is None:
+        _check(load().blockint8_moe_gemm(*args))
+    else:
+        _check(load().blockint8_moe_gemm_variant(int(variant), *args))
     return y
 
 

@@ -118,23 +118,45 @@ int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int32_t blockint8_gemm_select(int64_t M, int64_t N, int64_t K) {
+    return static_cast<int32_t>(bi8::select_gemm_path(M, N, K));
+}
+
+int32_t blockint8_moe_gemm_select(int64_t R, int64_t N, int64_t K, int32_t E) {
+    return static_cast<int32_t>(bi8::select_moe_gemm_path(R, N, K, E));
+}
+
+int32_t blockint8_gemm_variant(int32_t variant, const int8_t *xq, const float *xs,
+                               const int8_t *w, const float *ws, const uint16_t *bias,
+                               uint16_t *y, int64_t M, int64_t N, int64_t K, int32_t block_n,
+                               int32_t block_k, void *stream) {
+    static const char fn[] = "blockint8_gemm";
+    if (variant < BI8_GEMM_AUTO || variant > BI8_GEMM_TILE_256X256)
+        return fail(BI8_ERR_SHAPE, "%s: unknown kernel variant %d", fn, variant);
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, M, N, K, block_n, block_k);
+    if (s) return s;
+    if (variant == BI8_GEMM_SKINNY && M > 32)
+        return fail(BI8_ERR_SHAPE, "%s: the skinny kernel takes M <= 32, got %lld", fn, (long long)M);
+    if (M == 0) return ok();
+    if (bias && !aligned(bias, 2)) return fail(BI8_ERR_ALIGN, "%s: bias must be 2-byte aligned", fn);
+    return hip_status(fn, bi8::launch_gemm(static_cast<bi8::GemmPath>(variant), xq, xs, w, ws, bias,
+                                           y, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
 int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
                        const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
                        int32_t block_n, int32_t block_k, void *stream) {
-    static const char fn[] = "blockint8_gemm";
-    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, M, N, K, block_n, block_k);
-    if (s) return s;
-    if (M == 0) return ok();
-    if (bias && !aligned(bias, 2)) return fail(BI8_ERR_ALIGN, "%s: bias must be 2-byte aligned", fn);
-    const bi8::GemmPath path = bi8::select_gemm_path(M, N, K);
-    return hip_status(fn, bi8::launch_gemm(path, xq, xs, w, ws, bias, y, M, N, K,
-                                           static_cast<hipStream_t>(stream)));
+    return blockint8_gemm_variant(BI8_GEMM_AUTO, xq, xs, w, ws, bias, y, M, N, K, block_n, block_k,
+                                  stream);
 }
 
-int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
-                           const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
-                           int64_t K, int32_t E, int32_t block_n, int32_t block_k, void *stream) {
+int32_t blockint8_moe_gemm_variant(int32_t variant, const int8_t *xq, const float *xs,
+                                   const int32_t *expert_offsets, const int8_t *w,
+                                   const float *ws, uint16_t *y, int64_t R, int64_t N, int64_t K,
+                                   int32_t E, int32_t block_n, int32_t block_k, void *stream) {
     static const char fn[] = "blockint8_moe_gemm";
+    if (variant != BI8_GEMM_AUTO && variant != BI8_GEMM_TILE_256X128 && variant != BI8_GEMM_TILE_256X256)
+        return fail(BI8_ERR_SHAPE, "%s: kernel variant %d does not run the grouped GEMM", fn, variant);
     if (E <= 0 || E > 65536) return fail(BI8_ERR_SHAPE, "%s: E = %d out of range [1, 65536]", fn, E);
     int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, R, N, K, block_n, block_k);
     if (s) return s;
@@ -142,8 +164,16 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
     if (!expert_offsets) return fail(BI8_ERR_NULL, "%s: NULL expert_offsets", fn);
     if (!aligned(expert_offsets, 4))
         return fail(BI8_ERR_ALIGN, "%s: expert_offsets must be 4-byte aligned", fn);
-    return hip_status(fn, bi8::launch_moe_gemm(xq, xs, expert_offsets, w, ws, y, R, N, K, E,
+    return hip_status(fn, bi8::launch_moe_gemm(static_cast<bi8::GemmPath>(variant), xq, xs,
+                                               expert_offsets, w, ws, y, R, N, K, E,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
+                           const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
+                           int64_t K, int32_t E, int32_t block_n, int32_t block_k, void *stream) {
+    return blockint8_moe_gemm_variant(BI8_GEMM_AUTO, xq, xs, expert_offsets, w, ws, y, R, N, K, E,
+                                      block_n, block_k, stream);
 }
 
 }  // extern "C"

@@ -515,11 +515,230 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// Wide tiled path: 256 weight rows x 256 activation rows per workgroup
+// ---------------------------------------------------------------------------
+//
+// Moving a tile's operands from L2 into LDS costs (BN + BM) * 128 bytes per K
+// block for BN * BM * 128 MACs, so the 256 x 256 tile moves a third fewer
+// bytes per MAC than 256 x 128.  Its 8 waves (a 2 x 4 grid, 128 weight rows x
+// 64 activation rows each, i.e. 4 x 2 sub-tiles of 32 x 32) cannot hold a
+// whole block's int32 sums next to the fp32 accumulators, so the rescale is
+// pipelined per sub-tile instead: while the MFMAs of sub-tile j run, the VALU
+// converts and rescales sub-tile j - 1 (two 16-register int32 buffers).  Two
+// 64 KB stages form the LDS ring: block kb + 1 is loaded while block kb is
+// computed.
+struct WideCfg {
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int WN = 2, WM = 4;      // wave grid
+    static constexpr int SA = 4, SB = 2;      // 32 x 32 sub-tiles per wave
+    static constexpr int kWaveN = 32 * SA;    // 128 weight rows: one scale block
+    static constexpr int kWaveM = 32 * SB;    // 64 activation rows
+    static constexpr int kBN = kWaveN * WN;   // 256
+    static constexpr int kBM = kWaveM * WM;   // 256
+    static constexpr int kXOff = kBN * 128;
+    static constexpr int kStageBytes = kXOff + kBM * 128;
+    static constexpr int kWLoads = kBN / 8 / kWaves;
+    static constexpr int kXLoads = kBM / 8 / kWaves;
+    static constexpr int kSB = 8;
+    static constexpr int kScaleLoads = kBM * kSB / 64 / kWaves;
+};
+
+template <bool MOE>
+__global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = WideCfg;
+    constexpr int SA = C::SA, SB = C::SB;
+    __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
+    __shared__ float xsl[2][C::kBM * C::kSB];
+
+    Tile t;
+    if (!decode_tile<C::kBN, C::kBM, MOE>(p, t)) return;
+    if (t.rows <= 0) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t K = p.K, KB = p.KB;
+
+    const int64_t wrows = p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * KB, clamp_bytes(t.rows * KB * 4));
+
+    // Load pieces as in the 3-stage kernel: piece q (1 KB) covers tile rows
+    // [8q, 8q+8), lane i lands at LDS row 8q + i/8, slot i%8, which holds K
+    // chunk slot ^ swz(row).
+    // Pieces q = wave + 8 j all have the parity of `wave`, so every piece of
+    // a lane uses the same chunk and its offsets differ by j * 64 rows.
+    const int r_in = lane >> 3;
+    const int chunk = 16 * ((lane & 7) ^ r_in ^ (wave & 1));
+    const uint32_t go = (uint32_t)((8 * wave + r_in) * K + chunk);
+    const uint32_t piece_stride = (uint32_t)(8 * C::kWaves * K);
+    float sv[C::kScaleLoads];
+    uint32_t sofs[C::kScaleLoads];   // byte offset of this lane's scale entry at kb = 0
+#pragma unroll
+    for (int j = 0; j < C::kScaleLoads; ++j) {
+        const int f = (wave * C::kScaleLoads + j) * 64 + lane;
+        sofs[j] = (uint32_t)(((f / C::kSB) * KB + (f & (C::kSB - 1))) * 4);
+    }
+
+    auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
+        const int64_t k0 = kb * kBlock;
+        const uint32_t kofs = (uint32_t)k0;
+        if ((kb & (C::kSB - 1)) == 0) {
+            // Entries past the last K block read the next row's scales (or
+            // zero past the end of xs): they are never used, so no check.
+#pragma unroll
+            for (int j = 0; j < C::kScaleLoads; ++j)
+                sv[j] = buf_load_f32(sr, sofs[j] + (uint32_t)kb * 4u);
+        }
+        const bool in_k = k0 + chunk < K;
+#pragma unroll
+        for (int j = 0; j < C::kWLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024), 16,
+                in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::kXLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
+                in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
+    };
+    auto store_scales = [&](const int64_t half) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < C::kScaleLoads; ++j)
+            xsl[half][(wave * C::kScaleLoads + j) * 64 + lane] = sv[j];
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // lgkmcnt(0)
+    };
+
+    const int wn = wave % C::WN, wm = wave / C::WN;
+    const int rr = lane & 31, hi = lane >> 5;
+    const int swz = (rr & 7) ^ ((rr >> 3) & 1);
+    int frag_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
+    const int wrow0 = (wn * C::kWaveN + rr) * 128;
+    const int xrow0 = C::kXOff + (wm * C::kWaveM + rr) * 128;
+    int srow[SB];
+#pragma unroll
+    for (int b = 0; b < SB; ++b) srow[b] = (wm * C::kWaveM + 32 * b + rr) * C::kSB;
+
+    int64_t nbw = (t.n0 + wn * C::kWaveN) / kBlock;
+    if (nbw > p.NB - 1) nbw = p.NB - 1;
+    const BI8_CONST float *ws_row = reinterpret_cast<const BI8_CONST float *>(
+        reinterpret_cast<uintptr_t>(t.ws + nbw * KB));
+
+    i32x16 zero16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) zero16[i] = 0;
+    f32x16 y[SA][SB];
+#pragma unroll
+    for (int a = 0; a < SA; ++a)
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[a][b][i] = 0.f;
+
+    auto rescale = [&](const i32x16 &acc, f32x16 &yv, float tb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) yv[i] = fmaf((float)acc[i], tb, yv[i]);
+    };
+
+    // One K block: sub-tiles in the order (a, b) = (0,0), (0,1), (1,0), ...;
+    // the rescale of each sub-tile is issued after the next sub-tile's MFMAs.
+    auto compute = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
+        i32x4 xf[SB][4];
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
+        float tb[SB];
+        const float wsv = ws_row[kb];
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+            tb[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))] * wsv;
+        i32x16 acc[2];
+#pragma unroll
+        for (int a = 0; a < SA; ++a) {
+            i32x4 wf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                wf[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int j = a * SB + b;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc[j & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[s], xf[b][s],
+                                                                         s == 0 ? zero16 : acc[j & 1], 0, 0, 0);
+                if (j > 0) {
+                    const int pa = (j - 1) / SB, pb = (j - 1) % SB;
+                    rescale(acc[(j - 1) & 1], y[pa][pb], tb[pb]);
+                }
+            }
+        }
+        rescale(acc[(SA * SB - 1) & 1], y[SA - 1][SB - 1], tb[SB - 1]);
+    };
+
+    issue(lds0, 0);
+    for (int64_t kb = 0; kb < KB; kb += 2) {
+        // block kb in lds0, block kb + 1 in lds1
+        wait_vmcnt<0>();
+        if ((kb & (C::kSB - 1)) == 0) store_scales((kb / C::kSB) & 1);
+        lds_barrier();
+        issue(lds1, kb + 1);
+        compute(lds0, kb);
+        if (kb + 1 >= KB) break;
+        wait_vmcnt<0>();
+        lds_barrier();
+        issue(lds0, kb + 2);
+        compute(lds1, kb + 1);
+    }
+    wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
+
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+        const int64_t ml = wm * C::kWaveM + b * 32 + rr;
+        if (ml >= t.rows) continue;
+        uint16_t *yrow = p.y + (t.m0 + ml) * p.N;
+#pragma unroll
+        for (int a = 0; a < SA; ++a) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t n = t.n0 + wn * C::kWaveN + a * 32 + 8 * i4 + 4 * hi;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = y[a][b][4 * i4 + e];
+                    if (p.bias && n + e < p.N) v[e] += bf16_bits_to_f32(p.bias[n + e]);
+                }
+                if (p.wide_store) {
+                    if (n < p.N) {
+                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                }
+            }
+        }
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 // Explicit instantiations: the host pass must emit a launch stub for every
 // variant launched below.
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true>(GemmArgs);
+template __global__ void gemm_wide_kernel<false>(GemmArgs);
+template __global__ void gemm_wide_kernel<true>(GemmArgs);
 
 template <int WN, int WM, int SA, int SB, bool MOE, bool PING>
 hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
@@ -529,6 +748,16 @@ hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
     if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, SA, SB, MOE, PING>), dim3((unsigned)total), dim3(C::kThreads),
                        0, stream, p);
+    return hipGetLastError();
+}
+
+template <bool MOE>
+hipError_t launch_wide(GemmArgs p, hipStream_t stream) {
+    const int64_t total = p.tiles_m * p.tiles_n;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_wide_kernel<MOE>), dim3((unsigned)total), dim3(WideCfg::kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -554,17 +783,31 @@ GemmArgs make_args(const int8_t *xq, const float *xs, const int8_t *w, const flo
 
 }  // namespace
 
+// Tile choice: the 256 x 256 kernel moves the fewest bytes per MAC but needs
+// at least two rounds of workgroups over the 256 CUs to beat 256 x 128 (it has
+// half as many tiles); 128 x 64 keeps small problems spread over the chip.
 GemmPath select_gemm_path(int64_t M, int64_t N, int64_t K) {
     (void)K;
     if (M <= 32) return GemmPath::kSkinny;
-    const int64_t large_tiles = ((M + 127) / 128) * ((N + 255) / 256);
-    return large_tiles >= 256 ? GemmPath::kTiledLarge : GemmPath::kTiledSmall;
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 512) return GemmPath::kTile256x256;
+    if (((M + 127) / 128) * ((N + 255) / 256) >= 256) return GemmPath::kTile256x128;
+    return GemmPath::kTile128x64;
+}
+
+// Grouped GEMM: the expert segments are ragged, so the tile count is taken
+// from the mean segment length.
+GemmPath select_moe_gemm_path(int64_t R, int64_t N, int64_t K, int32_t E) {
+    (void)K;
+    const int64_t rows_per_expert = E > 0 ? R / E : R;
+    const int64_t wide_tiles = (int64_t)E * ((rows_per_expert + 255) / 256) * ((N + 255) / 256);
+    return wide_tiles >= 512 ? GemmPath::kTile256x256 : GemmPath::kTile256x128;
 }
 
 hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const int8_t *w,
                        const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
     GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
+    if (path == GemmPath::kAuto) path = select_gemm_path(M, N, K);
     switch (path) {
         case GemmPath::kSkinny: {
             if (M > 32) return hipErrorInvalidValue;
@@ -579,27 +822,42 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
                                    dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
             return hipGetLastError();
         }
-        case GemmPath::kTiledLarge:
+        case GemmPath::kTile256x256:
+            p.tiles_m = (M + 255) / 256;
+            p.tiles_n = (N + 255) / 256;
+            return launch_wide<false>(p, stream);
+        case GemmPath::kTile256x128:
             p.tiles_m = (M + 127) / 128;
             p.tiles_n = (N + 255) / 256;
             return launch_tiled<4, 2, 2, 2, false, true>(p, stream);
-        case GemmPath::kTiledSmall:
+        case GemmPath::kTile128x64:
             p.tiles_m = (M + 63) / 64;
             p.tiles_n = (N + 127) / 128;
             return launch_tiled<4, 2, 1, 1, false, true>(p, stream);
+        default:
+            return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
 }
 
-hipError_t launch_moe_gemm(const int8_t *xq, const float *xs, const int32_t *offsets,
+hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, const int32_t *offsets,
                            const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
                            int64_t K, int32_t E, hipStream_t stream) {
     GemmArgs p = make_args(xq, xs, w, ws, nullptr, y, R, N, K);
     p.offsets = offsets;
     p.E = E;
-    p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
-    p.tiles_n = (N + 255) / 256;
-    return launch_tiled<4, 2, 2, 2, true, true>(p, stream);
+    if (path == GemmPath::kAuto) path = select_moe_gemm_path(R, N, K, E);
+    switch (path) {
+        case GemmPath::kTile256x256:
+            p.tiles_m = (R + 255) / 256 + E;   // >= sum over experts of ceil(rows_e / 256)
+            p.tiles_n = (N + 255) / 256;
+            return launch_wide<true>(p, stream);
+        case GemmPath::kTile256x128:
+            p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
+            p.tiles_n = (N + 255) / 256;
+            return launch_tiled<4, 2, 2, 2, true, true>(p, stream);
+        default:
+            return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace bi8

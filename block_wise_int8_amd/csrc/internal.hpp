@@ -7,10 +7,12 @@
 
 namespace bi8 {
 
-// Kernel paths for the dense GEMM, chosen by shape in select_gemm_path().
-enum class GemmPath : int { kSkinny = 0, kTiledLarge = 1, kTiledSmall = 2 };
+// GEMM kernels (the values are the BI8_GEMM_* variant ids of the C ABI).
+enum class GemmPath : int { kAuto = 0, kSkinny = 1, kTile128x64 = 2, kTile256x128 = 3, kTile256x256 = 4 };
 
+// Shape-based choice for the dense and the grouped GEMM (never kAuto).
 GemmPath select_gemm_path(int64_t M, int64_t N, int64_t K);
+GemmPath select_moe_gemm_path(int64_t R, int64_t N, int64_t K, int32_t E);
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *xq,
                             float *xs, hipStream_t stream);
@@ -19,7 +21,7 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
                        const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
 
-hipError_t launch_moe_gemm(const int8_t *xq, const float *xs, const int32_t *offsets,
+hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, const int32_t *offsets,
                            const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
                            int64_t K, int32_t E, hipStream_t stream);
 

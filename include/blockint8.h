@@ -137,6 +137,46 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
                            int64_t R, int64_t N, int64_t K, int32_t E,
                            int32_t block_n, int32_t block_k, void *stream);
 
+/*
+ * Kernel variants.  blockint8_gemm and blockint8_moe_gemm choose a kernel by
+ * shape; the *_variant entry points run a named one instead, with the same
+ * arguments, results and errors, so that every kernel can be checked and
+ * timed on any shape it accepts.  A variant that cannot run the shape
+ * (BI8_GEMM_SKINNY with more than 32 rows, BI8_GEMM_SKINNY or
+ * BI8_GEMM_TILE_128X64 for the grouped GEMM) returns BI8_ERR_SHAPE; an
+ * unknown variant id returns BI8_ERR_SHAPE.
+ *
+ *   BI8_GEMM_AUTO          the shape-based choice
+ *   BI8_GEMM_SKINNY        M <= 32: weight rows streamed into registers
+ *   BI8_GEMM_TILE_128X64   128 weight rows x 64 activation rows per workgroup
+ *   BI8_GEMM_TILE_256X128  256 x 128
+ *   BI8_GEMM_TILE_256X256  256 x 256
+ */
+enum {
+    BI8_GEMM_AUTO = 0,
+    BI8_GEMM_SKINNY = 1,
+    BI8_GEMM_TILE_128X64 = 2,
+    BI8_GEMM_TILE_256X128 = 3,
+    BI8_GEMM_TILE_256X256 = 4
+};
+
+/* The variant blockint8_gemm runs for an M x N x K problem (M, N, K > 0). */
+int32_t blockint8_gemm_select(int64_t M, int64_t N, int64_t K);
+
+/* The variant blockint8_moe_gemm runs for R rows over E experts. */
+int32_t blockint8_moe_gemm_select(int64_t R, int64_t N, int64_t K, int32_t E);
+
+int32_t blockint8_gemm_variant(int32_t variant, const int8_t *xq, const float *xs,
+                               const int8_t *w, const float *ws, const uint16_t *bias,
+                               uint16_t *y, int64_t M, int64_t N, int64_t K,
+                               int32_t block_n, int32_t block_k, void *stream);
+
+int32_t blockint8_moe_gemm_variant(int32_t variant, const int8_t *xq, const float *xs,
+                                   const int32_t *expert_offsets, const int8_t *w,
+                                   const float *ws, uint16_t *y, int64_t R, int64_t N,
+                                   int64_t K, int32_t E, int32_t block_n, int32_t block_k,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

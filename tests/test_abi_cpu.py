@@ -37,7 +37,9 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
-                          "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm"}
+                          "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm",
+                          "blockint8_gemm_select", "blockint8_moe_gemm_select",
+                          "blockint8_gemm_variant", "blockint8_moe_gemm_variant"}
     for name in names:
         assert hasattr(lib, name), name
     # exported with C linkage (no mangling) in the shared object
@@ -136,3 +138,62 @@ def test_binding_has_no_cpu_path():
 def test_scale_shape_helper():
     assert bi8.scale_shape(4096, 4096) == (32, 32)
     assert bi8.scale_shape(5000, 4000) == (40, 32)
+
+
+def test_variant_ids_match_header():
+    text = open(HEADER).read()
+    ids = dict((k, int(v)) for k, v in re.findall(r"\b(BI8_GEMM_\w+)\s*=\s*(\d+)", text))
+    assert ids == {"BI8_GEMM_AUTO": bi8.GEMM_AUTO, "BI8_GEMM_SKINNY": bi8.GEMM_SKINNY,
+                   "BI8_GEMM_TILE_128X64": bi8.GEMM_TILE_128X64,
+                   "BI8_GEMM_TILE_256X128": bi8.GEMM_TILE_256X128,
+                   "BI8_GEMM_TILE_256X256": bi8.GEMM_TILE_256X256}
+
+
+@pytest.mark.parametrize("M,N,K,variant", [
+    (1, 4096, 4096, bi8.GEMM_SKINNY), (32, 100, 128, bi8.GEMM_SKINNY),
+    (33, 4096, 4096, bi8.GEMM_TILE_128X64), (333, 5000, 4000, bi8.GEMM_TILE_128X64),
+    (2048, 4096, 14336, bi8.GEMM_TILE_256X128), (4096, 4096, 4096, bi8.GEMM_TILE_256X128),
+    (2048, 28672, 4096, bi8.GEMM_TILE_256X256), (8192, 8192, 1024, bi8.GEMM_TILE_256X256),
+])
+def test_gemm_select(lib, M, N, K, variant):
+    """The shape-based choice (a host function: no launch)."""
+    assert bi8.gemm_select(M, N, K) == variant
+
+
+def test_moe_gemm_select(lib):
+    assert bi8.moe_gemm_select(8192, 28672, 4096, 8) == bi8.GEMM_TILE_256X256
+    assert bi8.moe_gemm_select(8192, 4096, 14336, 8) == bi8.GEMM_TILE_256X256
+    assert bi8.moe_gemm_select(512, 4096, 4096, 8) == bi8.GEMM_TILE_256X128
+
+
+def gemm_v(lib, variant, M=4, xq=P16, **kw):
+    a = dict(xs=P16, w=P16, ws=P16, bias=None, y=P16, N=256, K=256, bn=128, bk=128)
+    a.update(kw)
+    return lib.blockint8_gemm_variant(variant, xq, a["xs"], a["w"], a["ws"], a["bias"], a["y"], M,
+                                      a["N"], a["K"], a["bn"], a["bk"], None)
+
+
+@pytest.mark.parametrize("variant,M,kw,status", [
+    (-1, 4, {}, SHAPE), (5, 4, {}, SHAPE), (99, 4, {}, SHAPE),
+    (bi8.GEMM_SKINNY, 33, {}, SHAPE),                       # skinny takes M <= 32
+    (bi8.GEMM_TILE_256X256, 64, dict(xq=None), NULL),
+    (bi8.GEMM_TILE_256X128, 64, dict(bk=64), BLOCK),
+    (bi8.GEMM_TILE_128X64, 64, dict(K=72), ALIGN),
+])
+def test_gemm_variant_rejects(lib, variant, M, kw, status):
+    assert gemm_v(lib, variant, M=M, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_gemm")
+
+
+def test_gemm_variant_empty_is_noop(lib):
+    for v in range(5):
+        assert gemm_v(lib, v, M=0, xq=None, xs=None, w=None, ws=None, y=None) == OK
+
+
+@pytest.mark.parametrize("variant,status", [
+    (bi8.GEMM_SKINNY, SHAPE), (bi8.GEMM_TILE_128X64, SHAPE), (7, SHAPE), (-2, SHAPE),
+])
+def test_moe_gemm_variant_rejects(lib, variant, status):
+    assert lib.blockint8_moe_gemm_variant(variant, P16, P16, P16, P16, P16, P16, 4, 256, 256, 2, 128,
+                                          128, None) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_moe_gemm")

@@ -98,10 +98,13 @@ def test_quant_row_stride():
 
 # ------------------------------------------------------------------- gemm --
 
-def run_gemm(xq, xs, w, ws, bias=None):
+def run_gemm(xq, xs, w, ws, bias=None, variant=None):
     y = bi8.gemm(to_dev(xq), to_dev(xs), to_dev(w), to_dev(ws),
-                 None if bias is None else bf16_to_dev(bias))
+                 None if bias is None else bf16_to_dev(bias), variant=variant)
     return bf16_bits(y)
+
+
+TILED = [bi8.GEMM_TILE_128X64, bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]
 
 
 SHAPES = [
@@ -121,6 +124,20 @@ def test_gemm_shapes_vs_oracle(M, N, K):
     y_ref = oracle.gemm(xq, xs, w, ws)
     y = run_gemm(xq, xs, w, ws)
     assert_gemm_close(y, y_ref, "M=%d N=%d K=%d" % (M, N, K))
+    variants = TILED + ([bi8.GEMM_SKINNY] if M <= 32 else [])
+    for v in variants:
+        assert_gemm_close(run_gemm(xq, xs, w, ws, variant=v), y_ref, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
+
+
+# Shapes spanning several tiles of every tiled kernel, with ragged M, N and K
+# tails, including a tile row with a single valid activation row.
+@pytest.mark.parametrize("M,N,K", [(513, 520, 1040), (769, 1000, 400), (257, 2056, 272)])
+def test_gemm_tiled_variants_multi_tile(M, N, K):
+    x, w, ws = make_case((M, N, K, 7), M, N, K)
+    xq, xs = oracle.quant_act(x)
+    y_ref = oracle.gemm(xq, xs, w, ws)
+    for v in TILED:
+        assert_gemm_close(run_gemm(xq, xs, w, ws, variant=v), y_ref, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "ragged", "prefill", "gate_up", "down"])
@@ -208,6 +225,9 @@ def test_gemm_empty_and_errors():
 
 # -------------------------------------------------------------------- moe --
 
+MOE_VARIANTS = [None, bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]
+
+
 def moe_case(seed, counts, N, K):
     rng = np.random.default_rng(seed)
     E = len(counts)
@@ -226,19 +246,22 @@ def moe_case(seed, counts, N, K):
     ([0, 0, 128], 128, 128),
     ([300, 5, 33, 128, 129], 512, 1024),
 ])
-def test_moe_small_vs_oracle(counts, N, K):
+@pytest.mark.parametrize("variant", MOE_VARIANTS)
+def test_moe_small_vs_oracle(counts, N, K, variant):
     x, off, w, ws = moe_case(len(counts) * 100 + N, counts, N, K)
     xq, xs = oracle.quant_act(x)
     y_ref = oracle.moe_gemm(xq, xs, off, w, ws)
-    y = bf16_bits(bi8.moe_gemm(to_dev(xq), to_dev(xs), to_dev(off), to_dev(w), to_dev(ws)))
-    assert_gemm_close(y, y_ref, "moe %s" % counts)
+    y = bf16_bits(bi8.moe_gemm(to_dev(xq), to_dev(xs), to_dev(off), to_dev(w), to_dev(ws),
+                               variant=variant))
+    assert_gemm_close(y, y_ref, "moe %s variant %s" % (counts, variant))
 
 
-def test_moe_one_expert_equals_dense_gemm():
+@pytest.mark.parametrize("variant", [bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256])
+def test_moe_one_expert_equals_dense_gemm(variant):
     x, off, w, ws = moe_case(7, [500], 640, 512)
     xq, xs = to_dev(oracle.quant_act(x)[0]), to_dev(oracle.quant_act(x)[1])
-    y_moe = bf16_bits(bi8.moe_gemm(xq, xs, to_dev(off), to_dev(w), to_dev(ws)))
-    y_dense = bf16_bits(bi8.gemm(xq, xs, to_dev(w[0]), to_dev(ws[0])))
+    y_moe = bf16_bits(bi8.moe_gemm(xq, xs, to_dev(off), to_dev(w), to_dev(ws), variant=variant))
+    y_dense = bf16_bits(bi8.gemm(xq, xs, to_dev(w[0]), to_dev(ws[0]), variant=variant))
     assert np.array_equal(y_moe, y_dense)
 
 
@@ -258,9 +281,12 @@ def test_moe_workload_vs_oracle():
 
     dev_off = to_dev(off)
     xq1, xs1 = bi8.quant_act(bf16_to_dev(x[tok]))
-    y13 = bf16_bits(bi8.moe_gemm(xq1, xs1, dev_off, to_dev(w13), to_dev(ws13)))
     xq2, xs2 = bi8.quant_act(bf16_to_dev(x2))
-    y2 = bf16_bits(bi8.moe_gemm(xq2, xs2, dev_off, to_dev(w2), to_dev(ws2)))
+    w13_d, ws13_d, w2_d, ws2_d = to_dev(w13), to_dev(ws13), to_dev(w2), to_dev(ws2)
+    outs = {}
+    for v in MOE_VARIANTS:
+        outs[v] = (bf16_bits(bi8.moe_gemm(xq1, xs1, dev_off, w13_d, ws13_d, variant=v)),
+                   bf16_bits(bi8.moe_gemm(xq2, xs2, dev_off, w2_d, ws2_d, variant=v)))
 
     srng = np.random.default_rng(3)
     for e in range(E):
@@ -270,6 +296,9 @@ def test_moe_workload_vs_oracle():
         rows = a + sample_rows(b - a, 3, srng)
         q1, s1 = oracle.quant_act(x[tok[rows]])
         assert np.array_equal(xq1.cpu().numpy()[rows], q1)
-        assert_gemm_close(y13[rows], oracle.gemm(q1, s1, w13[e], ws13[e]), "w13 e=%d" % e)
+        ref13 = oracle.gemm(q1, s1, w13[e], ws13[e])
         q2, s2 = oracle.quant_act(x2[rows])
-        assert_gemm_close(y2[rows], oracle.gemm(q2, s2, w2[e], ws2[e]), "w2 e=%d" % e)
+        ref2 = oracle.gemm(q2, s2, w2[e], ws2[e])
+        for v, (y13, y2) in outs.items():
+            assert_gemm_close(y13[rows], ref13, "w13 e=%d variant %s" % (e, v))
+            assert_gemm_close(y2[rows], ref2, "w2 e=%d variant %s" % (e, v))
