@@ -73,7 +73,9 @@ def load() -> ctypes.CDLL:
     lib.blockint8_moe_gemm_select.argtypes = [i64, i64, i64, i32]
     lib.blockint8_gemm_variant.argtypes = [i32] + lib.blockint8_gemm.argtypes
     lib.blockint8_moe_gemm_variant.argtypes = [i32] + lib.blockint8_moe_gemm.argtypes
-    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_gemm_select",
+    lib.blockint8_linear.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
+    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_linear",
+              "blockint8_gemm_select",
               "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -225,7 +227,36 @@ def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tensor | None = None,
-           block=(BLOCK, BLOCK)) -> torch.Tensor:
-    """Block-wise INT8 linear with dynamic activation scales: quant_act then gemm."""
-    xq, xs = quant_act(x, block_k=block[1])
-    return gemm(xq, xs, w, ws, bias=bias, block=block)
+           y: torch.Tensor | None = None, block=(BLOCK, BLOCK)) -> torch.Tensor:
+    """Block-wise INT8 linear with dynamic activation scales -> bf16 [M, N]:
+    quant_act into scratch tensors, then gemm, through one C call."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a 2-D bfloat16 tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device; there is no CPU path")
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    _need(w, "w", torch.int8, 2)
+    _need(ws, "ws", torch.float32, 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] with K = %d (got %s)" % (K, tuple(w.shape)))
+    NB, KB = scale_shape(N, K, *block)
+    if tuple(ws.shape) != (NB, KB):
+        raise ValueError("ws must be [%d, %d]" % (NB, KB))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must be [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty((M, KB), dtype=torch.float32, device=x.device)
+    ldx = x.stride(0) if M > 1 else K
+    _check(load().blockint8_linear(_ptr(x), ldx, _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K,
+                                   block[0], block[1], _ptr(xq), _ptr(xs), _stream_handle(x.device)))
+    return y

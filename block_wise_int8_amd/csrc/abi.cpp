@@ -150,6 +150,35 @@ int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const
                                   stream);
 }
 
+int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws,
+                         const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                         int32_t block_n, int32_t block_k, int8_t *xq_workspace,
+                         float *xs_workspace, void *stream) {
+    static const char fn[] = "blockint8_linear";
+    if (M < 0 || M > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: M = %lld out of range", fn, (long long)M);
+    if (N <= 0 || N > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
+    int32_t s = check_k(fn, K);
+    if (s) return s;
+    if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
+    if ((s = check_block(fn, block_n, block_k))) return s;
+    if (M == 0) return ok();
+    if (!x || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!xq_workspace || !xs_workspace) return fail(BI8_ERR_NULL, "%s: NULL workspace pointer", fn);
+    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
+    if (!aligned(x, 16) || !aligned(w, 16))
+        return fail(BI8_ERR_ALIGN, "%s: x and w must be 16-byte aligned", fn);
+    if (!aligned(ws, 4)) return fail(BI8_ERR_ALIGN, "%s: ws must be 4-byte aligned", fn);
+    if (!aligned(y, 2) || (bias && !aligned(bias, 2)))
+        return fail(BI8_ERR_ALIGN, "%s: y and bias must be 2-byte aligned", fn);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!aligned(xq_workspace, 16) || !aligned(xs_workspace, 4))
+        return fail(BI8_ERR_ALIGN, "%s: xq workspace must be 16-byte and xs workspace 4-byte aligned", fn);
+    hipError_t e = bi8::launch_quant_act(x, M, K, ldx, xq_workspace, xs_workspace, st);
+    if (e == hipSuccess)
+        e = bi8::launch_gemm(bi8::GemmPath::kAuto, xq_workspace, xs_workspace, w, ws, bias, y, M, N, K, st);
+    return hip_status(fn, e);
+}
+
 int32_t blockint8_moe_gemm_variant(int32_t variant, const int8_t *xq, const float *xs,
                                    const int32_t *expert_offsets, const int8_t *w,
                                    const float *ws, uint16_t *y, int64_t R, int64_t N, int64_t K,

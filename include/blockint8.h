@@ -138,6 +138,29 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
                            int32_t block_n, int32_t block_k, void *stream);
 
 /*
+ * Dynamic-scale block-wise INT8 linear in one call: the activations are
+ * quantised at run time (blockint8_quant_act) and fed to the block-scaled
+ * GEMM (blockint8_gemm).  Section 4 of the page: the linear takes the input,
+ * the int8 weight, its block scales and an optional bias, and with no input
+ * scale it computes the per-token activation scales itself.
+ *
+ *   x             bf16 [M, ldx]; row stride ldx >= K elements, ldx % 8 == 0
+ *   w, ws, bias, y, block_n, block_k: as blockint8_gemm
+ *   xq_workspace  int8 [M, K]           caller-owned; hold the quantised
+ *   xs_workspace  fp32 [M, ceil(K/128)] activations on return
+ *
+ * Two launches on the stream (quantisation, then the GEMM); y equals
+ * blockint8_quant_act followed by blockint8_gemm exactly.
+ *
+ * Errors: as blockint8_quant_act and blockint8_gemm; NULL workspace ->
+ * BI8_ERR_NULL; workspace misaligned (xq 16 B, xs 4 B) -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws,
+                         const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                         int32_t block_n, int32_t block_k, int8_t *xq_workspace,
+                         float *xs_workspace, void *stream);
+
+/*
  * Kernel variants.  blockint8_gemm and blockint8_moe_gemm choose a kernel by
  * shape; the *_variant entry points run a named one instead, with the same
  * arguments, results and errors, so that every kernel can be checked and

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
                           "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm",
-                          "blockint8_gemm_select", "blockint8_moe_gemm_select",
+                          "blockint8_linear", "blockint8_gemm_select", "blockint8_moe_gemm_select",
                           "blockint8_gemm_variant", "blockint8_moe_gemm_variant"}
     for name in names:
         assert hasattr(lib, name), name
@@ -197,3 +197,26 @@ def test_moe_gemm_variant_rejects(lib, variant, status):
     assert lib.blockint8_moe_gemm_variant(variant, P16, P16, P16, P16, P16, P16, 4, 256, 256, 2, 128,
                                           128, None) == status
     assert lib.blockint8_last_error().decode().startswith("blockint8_moe_gemm")
+
+
+def linear(lib, x=P16, ldx=256, w=P16, ws=P16, bias=None, y=P16, M=4, N=256, K=256, bn=128, bk=128,
+           xq=P16, xs=P16):
+    return lib.blockint8_linear(x, ldx, w, ws, bias, y, M, N, K, bn, bk, xq, xs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(ws=None), NULL), (dict(y=None), NULL),
+    (dict(xq=None), NULL), (dict(xs=None), NULL),
+    (dict(M=-1), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(ldx=128), SHAPE),
+    (dict(bk=64), BLOCK), (dict(bn=256), BLOCK),
+    (dict(K=136, ldx=136), ALIGN), (dict(ldx=260), ALIGN), (dict(x=P16 + 8), ALIGN),
+    (dict(w=P16 + 1), ALIGN), (dict(ws=P16 + 2), ALIGN), (dict(y=P_ODD), ALIGN), (dict(bias=P_ODD), ALIGN),
+    (dict(xq=P16 + 4), ALIGN), (dict(xs=P16 + 1), ALIGN),
+])
+def test_linear_rejects(lib, kw, status):
+    assert linear(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_linear")
+
+
+def test_linear_empty_is_noop(lib):
+    assert linear(lib, M=0, x=None, w=None, ws=None, y=None, xq=None, xs=None) == OK

@@ -204,6 +204,28 @@ def test_linear_pipeline_matches_oracle():
     assert_gemm_close(y, oracle.gemm(xq, xs, w, ws), "linear")
 
 
+@pytest.mark.parametrize("M,N,K,ldx", [
+    (1, 256, 256, 256), (5, 300, 4000, 4000), (16, 1000, 1040, 1048), (33, 512, 144, 152),
+    (200, 384, 1040, 1040),
+])
+def test_linear_equals_quant_then_gemm(M, N, K, ldx):
+    """One C call, bit-identical to quant_act + gemm, and within tolerance of
+    the oracle; x with a row stride, with and without bias."""
+    x, w, ws = make_case((M, N, K, 3), M, N, K, 0.01)
+    xd = torch.zeros((M, ldx), dtype=torch.bfloat16, device=device())
+    xd[:, :K] = bf16_to_dev(x)
+    wd, wsd = to_dev(w), to_dev(ws)
+    bias = wl.activations(np.random.default_rng(M), 1, N)[0]
+    for b in (None, bias):
+        bd = None if b is None else bf16_to_dev(b)
+        y_one = bf16_bits(bi8.linear(xd[:, :K], wd, wsd, bias=bd))
+        xq, xs = bi8.quant_act(xd[:, :K])
+        y_two = bf16_bits(bi8.gemm(xq, xs, wd, wsd, bias=bd))
+        assert np.array_equal(y_one, y_two)
+        q_ref, s_ref = oracle.quant_act(x)
+        assert_gemm_close(y_one, oracle.gemm(q_ref, s_ref, w, ws, bias=b), "linear M=%d" % M)
+
+
 def test_gemm_unaligned_output_rows():
     """N % 4 != 0 takes the element-wise store path."""
     M, N, K = 70, 333, 256
