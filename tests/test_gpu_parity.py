@@ -110,7 +110,7 @@ TILED = [bi8.GEMM_TILE_128X64, bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]
 SHAPES = [
     # skinny path (M <= 32)
     (1, 16, 16), (1, 256, 256), (8, 4096, 512), (8, 100, 4000), (16, 300, 144), (17, 257, 1040),
-    (32, 512, 384), (5, 1000, 4096),
+    (32, 512, 384), (5, 1000, 4096), (32, 100, 2000), (31, 64, 2096), (3, 40, 21840),
     # tiled small and large paths, ragged N / K / M
     (33, 256, 256), (64, 128, 128), (100, 1000, 272), (129, 384, 400), (333, 500, 4000),
     (256, 2048, 256), (300, 5000, 128), (200, 7, 128), (1000, 16, 64), (513, 1024, 1024),
