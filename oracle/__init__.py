@@ -52,8 +52,13 @@ def _load():
     lib.oracle_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64]
     lib.oracle_gemm_f64.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64]
     lib.oracle_moe_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]
+    lib.oracle_topk_softmax.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp, vp]
+    lib.oracle_moe_align.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.oracle_silu_mul.argtypes = [vp, i64, i64, vp]
+    lib.oracle_combine.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp]
     for f in ("oracle_scale_shape", "oracle_quant_act", "oracle_gemm", "oracle_gemm_f64",
-              "oracle_moe_gemm"):
+              "oracle_moe_gemm", "oracle_topk_softmax", "oracle_moe_align", "oracle_silu_mul",
+              "oracle_combine"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -146,3 +151,54 @@ def moe_gemm(xq, xs, offsets, w, ws, block=(128, 128)) -> np.ndarray:
     _check(_load().oracle_moe_gemm(_ptr(xq), _ptr(xs), _ptr(off), _ptr(w), _ptr(ws), _ptr(y),
                                    R, N, K, E, block[0], block[1]), "moe_gemm")
     return y
+
+
+# ------------------------------------------------------------ MoE steps --
+
+def topk_softmax(logits, k: int, renorm: bool = False):
+    """Router: top-k of the binary64 softmax of fp32 logits [T, E].
+
+    Returns (ids int32 [T, k] in pick order, weights float64 [T, k]); ties
+    go to the lower expert; ``renorm`` divides the k weights by their sum."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float64)
+    _check(_load().oracle_topk_softmax(_ptr(lg), T, E, k, int(bool(renorm)), _ptr(ids), _ptr(w)),
+           "topk_softmax")
+    return ids, w
+
+
+def moe_align(ids, E: int):
+    """Dispatch order of the rows (t, slot), stable by (expert, t, slot).
+
+    Returns (sorted_token int32 [T*k], offsets int32 [E+1], row_of int32 [T, k])."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    st = np.zeros(T * k, np.int32)
+    off = np.zeros(E + 1, np.int32)
+    row_of = np.zeros((T, k), np.int32)
+    _check(_load().oracle_moe_align(_ptr(ids), T, k, E, _ptr(st), _ptr(off), _ptr(row_of)), "moe_align")
+    return st, off, row_of
+
+
+def silu_mul(h_bf16):
+    """a = bf16(silu(gate) * up) for h = [gate | up], bf16 bits [R, 2I] -> [R, I]."""
+    h = _c(h_bf16, np.uint16)
+    R, two_i = h.shape
+    I = two_i // 2
+    a = np.zeros((R, I), np.uint16)
+    _check(_load().oracle_silu_mul(_ptr(h), R, I, _ptr(a)), "silu_mul")
+    return a
+
+
+def combine(y2_bf16, row_of, weights):
+    """out[t] = bf16(sum_s w[t, s] * y2[row_of[t, s]]), bf16 bits [T, H]."""
+    y2 = _c(y2_bf16, np.uint16)
+    ro = _c(row_of, np.int32)
+    w = _c(weights, np.float32)
+    T, k = ro.shape
+    R, H = y2.shape
+    out = np.zeros((T, H), np.uint16)
+    _check(_load().oracle_combine(_ptr(y2), R, _ptr(ro), _ptr(w), T, k, H, _ptr(out)), "combine")
+    return out

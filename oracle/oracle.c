@@ -227,3 +227,122 @@ int oracle_moe_gemm(const int8_t *xq, const float *xs, const int32_t *off,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* O3: the MoE steps on either side of the grouped GEMM                 */
+/* ------------------------------------------------------------------ */
+
+/* Router.  [BW8] §6 hands dispatch and combine to the fused-MoE runner;
+ * the workload routes each token to the top k of the softmax of its router
+ * logits.  Per token t, in binary64:
+ *   p[e] = exp(l[e] - max_e l) / sum_e exp(l[e] - max_e l)  (sum ascending e)
+ *   the k largest p, picked one at a time (ties to the lower expert index),
+ *   weight = the chosen p, divided by the sum of the k chosen when renorm.
+ * logits fp32 [T, E]; ids int32 [T, k] in pick order; weights binary64 [T, k]. */
+int oracle_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t k, int renorm,
+                        int32_t *ids, double *weights)
+{
+    if (T < 0 || E <= 0 || k <= 0 || k > E || E > 4096) return -1;
+    if (T > 0 && (!logits || !ids || !weights)) return -1;
+    double p[4096];
+    unsigned char taken[4096];
+    for (int64_t t = 0; t < T; ++t) {
+        const float *l = logits + t * E;
+        double mx = -INFINITY;
+        for (int64_t e = 0; e < E; ++e) {
+            if (!isfinite(l[e])) return -2;
+            if ((double)l[e] > mx) mx = (double)l[e];
+        }
+        double sum = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - mx);
+            sum += p[e];
+        }
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] /= sum;
+            taken[e] = 0;
+        }
+        double chosen = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || p[e] > p[best])) best = e;
+            taken[best] = 1;
+            ids[t * k + j] = (int32_t)best;
+            weights[t * k + j] = p[best];
+            chosen += p[best];
+        }
+        if (renorm)
+            for (int64_t j = 0; j < k; ++j) weights[t * k + j] /= chosen;
+    }
+    return 0;
+}
+
+/* Dispatch order: the T*k rows (t, slot) sorted stably by (expert, t, slot),
+ * so that each expert's rows form one segment [offsets[e], offsets[e+1]).
+ * sorted_token int32 [T*k]: the token of each row; offsets int32 [E+1];
+ * row_of int32 [T*k]: the row that (t, slot) went to. */
+int oracle_moe_align(const int32_t *ids, int64_t T, int64_t k, int64_t E,
+                     int32_t *sorted_token, int32_t *offsets, int32_t *row_of)
+{
+    if (T < 0 || k <= 0 || E <= 0 || !offsets) return -1;
+    if (T > 0 && (!ids || !sorted_token || !row_of)) return -1;
+    for (int64_t i = 0; i < T * k; ++i)
+        if (ids[i] < 0 || ids[i] >= E) return -1;
+    int64_t r = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        offsets[e] = (int32_t)r;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t s = 0; s < k; ++s)
+                if (ids[t * k + s] == e) {
+                    sorted_token[r] = (int32_t)t;
+                    row_of[t * k + s] = (int32_t)r;
+                    ++r;
+                }
+    }
+    offsets[E] = (int32_t)r;
+    return 0;
+}
+
+/* Gate/up activation.  [BW8] §5: the MoE w13 weight is the gate and up
+ * projections fused, [2I, H], with 2 * ceil(I/bn) scale rows, so its output
+ * h [R, 2I] holds gate in columns [0, I) and up in [I, 2I) (gate first, the
+ * plainest reading).  The activation is SiLU gating, in binary64:
+ *   a[r, i] = bf16_rne( silu(gate) * up ),  silu(z) = z / (1 + exp(-z)). */
+int oracle_silu_mul(const uint16_t *h, int64_t R, int64_t I, uint16_t *a)
+{
+    if (R < 0 || I < 0) return -1;
+    if (R > 0 && I > 0 && (!h || !a)) return -1;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t i = 0; i < I; ++i) {
+            const double g = (double)bf16_bits_to_f32(h[r * 2 * I + i]);
+            const double u = (double)bf16_bits_to_f32(h[r * 2 * I + I + i]);
+            if (!isfinite(g) || !isfinite(u)) return -2;
+            const double silu = g / (1.0 + exp(-g));
+            a[r * I + i] = oracle_f64_to_bf16(silu * u);
+        }
+    return 0;
+}
+
+/* Combine: each token's output is the routing-weighted sum of its k expert
+ * rows, in binary64 with the slots in ascending order, rounded once:
+ *   out[t, :] = bf16_rne( sum_s w[t, s] * y2[row_of[t, s], :] ).
+ * y2 bf16 [R, H]; row_of int32 [T, k] in [0, R); w fp32 [T, k] (the weights
+ * the router produced). */
+int oracle_combine(const uint16_t *y2, int64_t R, const int32_t *row_of, const float *w,
+                   int64_t T, int64_t k, int64_t H, uint16_t *out)
+{
+    if (T < 0 || k <= 0 || H < 0 || R < 0) return -1;
+    if (T > 0 && H > 0 && (!y2 || !row_of || !w || !out)) return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < k; ++s) {
+                const int64_t r = row_of[t * k + s];
+                if (r < 0 || r >= R) return -1;
+                acc += (double)w[t * k + s] * (double)bf16_bits_to_f32(y2[r * H + c]);
+            }
+            out[t * H + c] = oracle_f64_to_bf16(acc);
+        }
+    return 0;
+}

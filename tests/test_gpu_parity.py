@@ -294,7 +294,8 @@ def test_moe_workload_vs_oracle():
     rng = wl.rng_for(c["seed"])
     x = wl.activations(rng, T, H)
     logits = wl.router_logits(rng, T, E)
-    tok, _, off = wl.dispatch_topk(logits, k)
+    ids, _ = oracle.topk_softmax(logits, k)
+    tok, off, _ = oracle.moe_align(ids, E)
     w13 = wl.weights(rng, E, 2 * I, H)
     ws13 = wl.weight_scales(rng, E, *oracle.scale_shape(2 * I, H))
     w2 = wl.weights(rng, E, H, I)

@@ -410,13 +410,134 @@ def test_moe_rejects_bad_offsets():
             oracle.moe_gemm(xq, xs, np.array(off, np.int32), w, ws)
 
 
+# ------------------------------------------------------- MoE steps (O3) --
+
+def test_topk_two_experts_is_the_logistic_function():
+    """E = 2, k = 1: the chosen weight is sigmoid(l_chosen - l_other) (scipy's expit)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(21)
+    lg = (rng.standard_normal((200, 2)) * 3).astype(np.float32)
+    ids, w = oracle.topk_softmax(lg, 1)
+    big = np.argmax(lg, axis=1)
+    assert np.array_equal(ids[:, 0], big)
+    d = lg[np.arange(200), big].astype(np.float64) - lg[np.arange(200), 1 - big].astype(np.float64)
+    np.testing.assert_allclose(w[:, 0], expit(d), rtol=1e-14)
+
+
+def test_topk_matches_library_softmax_and_brute_force_order():
+    from scipy.special import softmax
+    rng = np.random.default_rng(22)
+    lg = wl.router_logits(rng, 300, 8)
+    for k in (1, 2, 3, 8):
+        ids, w = oracle.topk_softmax(lg, k)
+        p = softmax(lg.astype(np.float64), axis=1)
+        for t in range(300):
+            order = sorted(range(8), key=lambda e: (-p[t, e], e))[:k]
+            assert list(ids[t]) == order
+        np.testing.assert_allclose(w, np.take_along_axis(p, ids.astype(np.int64), 1), rtol=1e-13)
+
+
+def test_topk_ties_go_to_the_lower_expert_and_shift_invariance():
+    lg = np.zeros((3, 8), np.float32)
+    lg[1, [2, 5]] = 1.0            # two equal maxima
+    lg[2] = [0, 3, 3, 3, 1, 1, 1, 1]
+    ids, w = oracle.topk_softmax(lg, 2)
+    assert ids.tolist() == [[0, 1], [2, 5], [1, 2]]
+    np.testing.assert_allclose(w[0], [1 / 8, 1 / 8], rtol=1e-15)
+    ids2, w2 = oracle.topk_softmax(lg + np.float32(50.0), 2)
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_allclose(w, w2, rtol=1e-13)
+
+
+def test_topk_renormalised_weights_sum_to_one():
+    lg = wl.router_logits(np.random.default_rng(23), 100, 8)
+    ids, w = oracle.topk_softmax(lg, 2, renorm=True)
+    ids0, w0 = oracle.topk_softmax(lg, 2)
+    assert np.array_equal(ids, ids0)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(w / w0, np.repeat((1 / w0.sum(1))[:, None], 2, axis=1), rtol=1e-12)
+
+
+def test_align_is_a_stable_sort_by_expert():
+    """Brute force: Python's sort on the key (expert, token, slot)."""
+    rng = np.random.default_rng(24)
+    for T, E, k in [(64, 8, 2), (7, 3, 1), (33, 16, 4), (1, 4, 2)]:
+        ids, _ = oracle.topk_softmax(wl.router_logits(rng, T, E), k)
+        st, off, row_of = oracle.moe_align(ids, E)
+        keys = sorted((int(ids[t, s]), t, s) for t in range(T) for s in range(k))
+        assert st.tolist() == [t for _, t, _ in keys]
+        counts = np.bincount(ids.ravel(), minlength=E)
+        assert off.tolist() == [0] + np.cumsum(counts).tolist()
+        for r, (e, t, s) in enumerate(keys):
+            assert row_of[t, s] == r and off[e] <= r < off[e + 1]
+
+
 def test_dispatch_layout_is_expert_sorted():
     rng = np.random.default_rng(17)
     logits = wl.router_logits(rng, 64, 8)
-    tok, slot, off = wl.dispatch_topk(logits, 2)
+    ids, _ = oracle.topk_softmax(logits, 2)
+    tok, off, _ = oracle.moe_align(ids, 8)
     assert off[0] == 0 and off[-1] == 128 and np.all(np.diff(off) >= 0)
     top2 = np.argsort(-logits, axis=1)[:, :2]
     for e in range(8):
         seg = tok[off[e]:off[e + 1]]
         assert np.all(np.diff(seg) >= 0)
         assert all(e in top2[t] for t in seg)
+
+
+def test_silu_mul_special_values_and_library_form():
+    """silu(z) * 1 against z * expit(z) (scipy); silu(0) = 0; silu(z) - silu(-z) = z."""
+    from scipy.special import expit
+    z = np.array([0.0, 1.0, -1.0, 2.5, -2.5, 10.0, -10.0, 80.0, -80.0, 0.001, -30000.0], np.float32)
+    zb = bf16_bits(z)
+    h = np.concatenate([zb[None, :], bf16_bits(np.ones_like(z))[None, :]], axis=1)
+    a = oracle.silu_mul(h)[0]
+    zf = bits_to_f32(zb).astype(np.float64)
+    ref = np.array([oracle.f64_to_bf16(v) for v in zf * expit(zf)], np.uint16)
+    assert np.array_equal(a, ref)
+    assert a[0] == 0 and bits_to_f32(a[1]) == bits_to_f32(bf16_bits([0.7310585786300049]))[0]
+    # odd part: silu(z) - silu(-z) = z, to bf16 rounding
+    for i in (1, 3, 5, 7):
+        np.testing.assert_allclose(bits_to_f32(a[i]) - bits_to_f32(a[i + 1]), zf[i], rtol=2 ** -7)
+
+
+def test_silu_mul_gate_up_order_and_scaling():
+    """Column i of the output uses gate column i and up column I + i; up scales linearly."""
+    rng = np.random.default_rng(25)
+    R, I = 5, 40
+    g = wl.activations(rng, R, I)
+    u = wl.activations(rng, R, I)
+    a = oracle.silu_mul(np.concatenate([g, u], axis=1))
+    a_swapped = oracle.silu_mul(np.concatenate([u, g], axis=1))
+    assert not np.array_equal(a, a_swapped)
+    two = bf16_bits(np.full((R, I), 2.0, np.float32))
+    a1 = oracle.silu_mul(np.concatenate([g, bf16_bits(np.ones((R, I), np.float32))], axis=1))
+    a2 = oracle.silu_mul(np.concatenate([g, two], axis=1))
+    assert np.array_equal(bits_to_f32(a2), 2 * bits_to_f32(a1))          # exact power-of-two scaling
+    from scipy.special import expit
+    gf = bits_to_f32(g).astype(np.float64)
+    uf = bits_to_f32(u).astype(np.float64)
+    np.testing.assert_allclose(bits_to_f32(a), gf * expit(gf) * uf, rtol=2 ** -8, atol=1e-30)
+
+
+def test_combine_special_cases():
+    rng = np.random.default_rng(26)
+    T, k, H = 6, 2, 24
+    ids, _ = oracle.topk_softmax(wl.router_logits(rng, T, 4), k)
+    _, _, row_of = oracle.moe_align(ids, 4)
+    y2 = wl.activations(rng, T * k, H)
+    # k = 1 with unit weight: a pure gather
+    out1 = oracle.combine(y2, row_of[:, :1], np.ones((T, 1), np.float32))
+    assert np.array_equal(out1, y2[row_of[:, 0]])
+    # equal rows and weights summing to one: the row itself
+    y_eq = y2.copy()
+    y_eq[row_of[:, 1]] = y_eq[row_of[:, 0]]
+    w = np.tile(np.array([[0.25, 0.75]], np.float32), (T, 1))
+    assert np.array_equal(oracle.combine(y_eq, row_of, w), y2[row_of[:, 0]])
+    # slot weights swap with the slots
+    w2 = rng.random((T, k)).astype(np.float32)
+    swapped = oracle.combine(y2, row_of[:, ::-1], w2[:, ::-1])
+    assert np.array_equal(swapped, oracle.combine(y2, row_of, w2))
+    # doubling the weights doubles the output exactly
+    assert np.array_equal(bits_to_f32(oracle.combine(y2, row_of, 2 * w2)),
+                          2 * bits_to_f32(oracle.combine(y2, row_of, w2)))
