@@ -12,6 +12,9 @@ Entry points (same names as the C ABI, without the ``blockint8_`` prefix):
 * :func:`gemm`       -- y = bf16(block-scaled int8 GEMM (+ bias)), [M, N]
 * :func:`moe_gemm`   -- the same per expert over expert-sorted rows
 * :func:`linear`     -- quant_act followed by gemm (the dynamic-scale linear)
+* :func:`moe_route`, :func:`quant_act_gather`, :func:`silu_mul_quant`,
+  :func:`moe_combine` -- the MoE steps around the grouped GEMM, and
+  :func:`moe_layer`, the whole FusedMoE layer built from them
 
 ``gemm`` and ``moe_gemm`` pick a kernel by shape (:func:`gemm_select`,
 :func:`moe_gemm_select`); their ``variant`` argument names one instead.
@@ -24,7 +27,8 @@ import os
 import torch
 
 __all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "moe_gemm",
-           "linear", "gemm_select", "moe_gemm_select", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
+           "linear", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
+           "silu_mul_quant", "moe_combine", "moe_layer", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
            "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
 
 BLOCK = 128
@@ -74,8 +78,13 @@ def load() -> ctypes.CDLL:
     lib.blockint8_gemm_variant.argtypes = [i32] + lib.blockint8_gemm.argtypes
     lib.blockint8_moe_gemm_variant.argtypes = [i32] + lib.blockint8_moe_gemm.argtypes
     lib.blockint8_linear.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
+    lib.blockint8_moe_route.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.blockint8_quant_act_gather.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, vp]
+    lib.blockint8_silu_mul_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    lib.blockint8_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, vp]
     for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_linear",
-              "blockint8_gemm_select",
+              "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_silu_mul_quant",
+              "blockint8_moe_combine", "blockint8_gemm_select",
               "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant"):
         getattr(lib, f).restype = i32
     _lib = lib
@@ -260,3 +269,100 @@ def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tenso
     _check(load().blockint8_linear(_ptr(x), ldx, _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K,
                                    block[0], block[1], _ptr(xq), _ptr(xs), _stream_handle(x.device)))
     return y
+
+
+# ----------------------------------------------------------------- MoE --
+
+def moe_route(logits: torch.Tensor, k: int, renormalize: bool = False):
+    """Top-k routing and dispatch order for fp32 router logits [T, E].
+
+    Returns ``(topk_ids int32 [T, k], topk_weights fp32 [T, k], sorted_token
+    int32 [T*k], expert_offsets int32 [E+1], row_of int32 [T, k])``."""
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    st = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check(load().blockint8_moe_route(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
+                                      _ptr(st), _ptr(off), _ptr(row_of), _stream_handle(dev)))
+    return ids, w, st, off, row_of
+
+
+def quant_act_gather(x: torch.Tensor, rows: torch.Tensor, xq: torch.Tensor | None = None,
+                     xs: torch.Tensor | None = None, block_k: int = BLOCK):
+    """quant_act of the rows ``x[rows]`` (bf16 [T, K], int32 indices [R])."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a 2-D bfloat16 tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device; there is no CPU path")
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    _need(rows, "rows", torch.int32, 1)
+    T, K = x.shape
+    R = rows.shape[0]
+    KB = (K + block_k - 1) // block_k
+    if xq is None:
+        xq = torch.empty((R, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((R, KB), dtype=torch.float32, device=x.device)
+    _need(xq, "xq", torch.int8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    ldx = x.stride(0) if T > 1 else K
+    _check(load().blockint8_quant_act_gather(_ptr(x), T, ldx, _ptr(rows), R, K, block_k, _ptr(xq), _ptr(xs),
+                                             _stream_handle(x.device)))
+    return xq, xs
+
+
+def silu_mul_quant(h: torch.Tensor, aq: torch.Tensor | None = None, as_: torch.Tensor | None = None,
+                   return_a: bool = False, block_k: int = BLOCK):
+    """h = [gate | up] bf16 [R, 2I] -> (aq int8 [R, I], as fp32 [R, ceil(I/128)][, a bf16 [R, I]])."""
+    _need(h, "h", torch.bfloat16, 2)
+    R, two_i = h.shape
+    if two_i % 2:
+        raise ValueError("h must have an even number of columns (gate | up)")
+    I = two_i // 2
+    IB = (I + block_k - 1) // block_k
+    if aq is None:
+        aq = torch.empty((R, I), dtype=torch.int8, device=h.device)
+    if as_ is None:
+        as_ = torch.empty((R, IB), dtype=torch.float32, device=h.device)
+    a = torch.empty((R, I), dtype=torch.bfloat16, device=h.device) if return_a else None
+    _check(load().blockint8_silu_mul_quant(_ptr(h), R, I, block_k, _ptr(aq), _ptr(as_), _ptr(a),
+                                           _stream_handle(h.device)))
+    return (aq, as_, a) if return_a else (aq, as_)
+
+
+def moe_combine(y2: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tensor,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """out[t] = bf16(sum_s w[t, s] * y2[row_of[t, s]]) -> bf16 [T, H]."""
+    _need(y2, "y2", torch.bfloat16, 2)
+    _need(row_of, "row_of", torch.int32, 2)
+    _need(topk_weights, "topk_weights", torch.float32, 2)
+    R, H = y2.shape
+    T, k = row_of.shape
+    if tuple(topk_weights.shape) != (T, k):
+        raise ValueError("topk_weights must be [T, k] like row_of")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y2.device)
+    _need(out, "out", torch.bfloat16, 2)
+    _check(load().blockint8_moe_combine(_ptr(y2), R, _ptr(row_of), _ptr(topk_weights), T, k, H, _ptr(out),
+                                        _stream_handle(y2.device)))
+    return out
+
+
+def moe_layer(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, ws13: torch.Tensor,
+              w2: torch.Tensor, ws2: torch.Tensor, k: int, renormalize: bool = False,
+              variant: int | None = None):
+    """The block-wise INT8 FusedMoE layer on the GPU, one launch per step:
+    route, gather + quantise, w13 grouped GEMM, SiLU gating + quantise, w2
+    grouped GEMM, weighted combine.  x bf16 [T, H]; logits fp32 [T, E];
+    w13 int8 [E, 2I, H]; w2 int8 [E, H, I].  Returns bf16 [T, H]."""
+    ids, w, st, off, row_of = moe_route(logits, k, renormalize)
+    xq, xs = quant_act_gather(x, st)
+    h = moe_gemm(xq, xs, off, w13, ws13, variant=variant)
+    aq, as_ = silu_mul_quant(h)
+    y2 = moe_gemm(aq, as_, off, w2, ws2, variant=variant)
+    return moe_combine(y2, row_of, w)

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libblockint8.so")
 
-SOURCES = ["abi.cpp", "quant_act.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "quant_act.hip", "gemm.hip", "moe.hip"]
 ARCH = "gfx950"
 
 

@@ -205,4 +205,77 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
                                       block_n, block_k, stream);
 }
 
+int32_t blockint8_moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renormalize,
+                            int32_t *topk_ids, float *topk_weights, int32_t *sorted_token,
+                            int32_t *expert_offsets, int32_t *row_of, void *stream) {
+    static const char fn[] = "blockint8_moe_route";
+    if (E < 1 || E > 1024) return fail(BI8_ERR_SHAPE, "%s: E = %d out of range [1, 1024]", fn, E);
+    if (k < 1 || k > 8 || k > E) return fail(BI8_ERR_SHAPE, "%s: k = %d out of range [1, min(E, 8)]", fn, k);
+    if (T < 0 || T * k > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: T = %lld out of range", fn, (long long)T);
+    if (!expert_offsets) return fail(BI8_ERR_NULL, "%s: NULL expert_offsets", fn);
+    if (T > 0 && (!logits || !topk_ids || !topk_weights || !sorted_token || !row_of))
+        return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned(expert_offsets, 4) ||
+        (T > 0 && (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+                   !aligned(sorted_token, 4) || !aligned(row_of, 4))))
+        return fail(BI8_ERR_ALIGN, "%s: pointers must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_moe_route(logits, T, E, k, renormalize, topk_ids, topk_weights,
+                                                sorted_token, expert_offsets, row_of,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, const int32_t *rows,
+                                   int64_t R, int64_t K, int32_t block_k, int8_t *xq, float *xs,
+                                   void *stream) {
+    static const char fn[] = "blockint8_quant_act_gather";
+    if (R < 0 || R > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: R = %lld out of range", fn, (long long)R);
+    if (T < 0) return fail(BI8_ERR_SHAPE, "%s: T = %lld < 0", fn, (long long)T);
+    int32_t s = check_k(fn, K);
+    if (s) return s;
+    if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
+    if ((s = check_block(fn, 128, block_k))) return s;
+    if (R == 0) return ok();
+    if (!rows || !xq || !xs || (T > 0 && !x)) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
+    if ((x && !aligned(x, 16)) || !aligned(xq, 16))
+        return fail(BI8_ERR_ALIGN, "%s: x and xq must be 16-byte aligned", fn);
+    if (!aligned(xs, 4) || !aligned(rows, 4)) return fail(BI8_ERR_ALIGN, "%s: xs and rows must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_quant_act_gather(x, T, ldx, rows, R, K, xq, xs,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int32_t block_k, int8_t *aq,
+                                 float *as, uint16_t *a, void *stream) {
+    static const char fn[] = "blockint8_silu_mul_quant";
+    if (R < 0 || R > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: R = %lld out of range", fn, (long long)R);
+    int32_t s = check_k(fn, I);
+    if (s) return s;
+    if ((s = check_block(fn, 128, block_k))) return s;
+    if (R == 0) return ok();
+    if (!h || !aq || !as) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned(h, 16) || !aligned(aq, 16) || (a && !aligned(a, 16)))
+        return fail(BI8_ERR_ALIGN, "%s: h, aq and a must be 16-byte aligned", fn);
+    if (!aligned(as, 4)) return fail(BI8_ERR_ALIGN, "%s: as must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_silu_mul_quant(h, R, I, aq, as, a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_of,
+                              const float *topk_weights, int64_t T, int32_t k, int64_t H,
+                              uint16_t *out, void *stream) {
+    static const char fn[] = "blockint8_moe_combine";
+    if (T < 0 || R < 0 || R > kMaxRows || H <= 0 || H > kMaxRows || k < 1 || T * k > kMaxRows)
+        return fail(BI8_ERR_SHAPE, "%s: bad shape T = %lld, R = %lld, k = %d, H = %lld", fn, (long long)T,
+                    (long long)R, k, (long long)H);
+    if (H % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: H = %lld must be a multiple of 8", fn, (long long)H);
+    if (T == 0) return ok();
+    if (!row_of || !topk_weights || !out || (R > 0 && !y2))
+        return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if ((y2 && !aligned(y2, 16)) || !aligned(out, 16))
+        return fail(BI8_ERR_ALIGN, "%s: y2 and out must be 16-byte aligned", fn);
+    if (!aligned(row_of, 4) || !aligned(topk_weights, 4))
+        return fail(BI8_ERR_ALIGN, "%s: row_of and weights must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_moe_combine(y2, R, row_of, topk_weights, T, k, H, out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -17,6 +17,19 @@ GemmPath select_moe_gemm_path(int64_t R, int64_t N, int64_t K, int32_t E);
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *xq,
                             float *xs, hipStream_t stream);
 
+// Gather form: output row m quantises row rows[m] of x ([src_rows, ldx]).
+hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t ldx, const int32_t *rows,
+                                   int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream);
+
+// MoE steps around the grouped GEMM (E <= 1024, k <= 8).
+hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renorm,
+                            int32_t *ids, float *weights, int32_t *sorted_token, int32_t *offsets,
+                            int32_t *row_of, hipStream_t stream);
+hipError_t launch_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int8_t *aq, float *as,
+                                 uint16_t *a_out, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_of, const float *w,
+                              int64_t T, int32_t k, int64_t H, uint16_t *out, hipStream_t stream);
+
 hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const int8_t *w,
                        const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);

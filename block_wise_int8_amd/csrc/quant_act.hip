@@ -37,21 +37,25 @@ __device__ __forceinline__ int32_t quant_one(float x, float s) {
     return (int32_t)q;
 }
 
+// rows (gather form, may be null): output row m quantises source row
+// rows[m] of x (src_rows rows); an index outside [0, src_rows) reads zeros.
 __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     const uint16_t *__restrict__ x, int64_t K, int64_t ldx, int8_t *__restrict__ xq,
-    float *__restrict__ xs, int64_t KB, int64_t waves_per_row, int64_t total_waves) {
+    float *__restrict__ xs, int64_t KB, int64_t waves_per_row, int64_t total_waves,
+    const int32_t *__restrict__ rows, int64_t src_rows) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
     if (wave >= total_waves) return;
     const int64_t m = wave / waves_per_row;
     const int64_t g = (wave - m * waves_per_row) * kGroupsPerWave + (lane >> 4);
     const int64_t k = g * kBlock + (lane & 15) * 8;
+    const int64_t src = rows ? (int64_t)rows[m] : m;
     // K % 16 == 0, so a lane's 8 elements are either all inside the row or all
     // outside; outside lanes contribute zeros, which change no group max.
     const bool valid = (g < KB) && (k < K);
 
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (valid) v = *reinterpret_cast<const u32x4 *>(x + m * ldx + k);
+    if (valid && src >= 0 && src < src_rows) v = *reinterpret_cast<const u32x4 *>(x + src * ldx + k);
 
     float f[8];
 #pragma unroll
@@ -82,13 +86,19 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *xq,
                             float *xs, hipStream_t stream) {
+    return launch_quant_act_gather(x, M, ldx, nullptr, M, K, xq, xs, stream);
+}
+
+hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t ldx, const int32_t *rows,
+                                   int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream) {
     const int64_t KB = (K + kBlock - 1) / kBlock;
     const int64_t waves_per_row = (KB + kGroupsPerWave - 1) / kGroupsPerWave;
     const int64_t total_waves = M * waves_per_row;
     const int64_t blocks = (total_waves + kQuantWaves - 1) / kQuantWaves;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kQuantWaves * 64), 0, stream,
-                       x, K, ldx, xq, xs, KB, waves_per_row, total_waves);
+                       x, K, ldx, xq, xs, KB, waves_per_row, total_waves, rows, src_rows);
     return hipGetLastError();
 }
 

@@ -160,6 +160,90 @@ int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
                          int32_t block_n, int32_t block_k, int8_t *xq_workspace,
                          float *xs_workspace, void *stream);
 
+/* ---------------------------------------------------------------------
+ * The MoE steps on either side of the grouped GEMM (section 6 of the page:
+ * the fused-MoE runner routes the tokens, runs the per-expert int8 GEMMs and
+ * combines the expert outputs).  With them the whole FusedMoE layer runs on
+ * the GPU:
+ *
+ *   blockint8_moe_route          logits -> top-k ids and weights, dispatch
+ *                                order, expert_offsets, row_of
+ *   blockint8_quant_act_gather   x[sorted_token] -> int8 rows + scales
+ *   blockint8_moe_gemm           w13 (gate | up) per expert
+ *   blockint8_silu_mul_quant     silu(gate) * up -> int8 rows + scales
+ *   blockint8_moe_gemm           w2 per expert
+ *   blockint8_moe_combine        weighted sum of each token's k rows
+ * ------------------------------------------------------------------- */
+
+/*
+ * Router and dispatch order, two launches on the stream.
+ *
+ *   logits        fp32 [T, E] (device)
+ *   topk_ids      int32 [T, k]  out: the k experts with the largest softmax
+ *                 probability, in that order; ties go to the lower expert
+ *   topk_weights  fp32 [T, k]   out: their probabilities (divided by their
+ *                 sum when renormalize != 0)
+ *   sorted_token  int32 [T*k]   out: token of each dispatched row; rows are
+ *                 sorted stably by (expert, token)
+ *   expert_offsets int32 [E+1]  out: rows [off[e], off[e+1]) use expert e
+ *   row_of        int32 [T, k]  out: the row that (token, slot) went to
+ *
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 8), T * k < 2^31.  T == 0 writes
+ * expert_offsets (all zero).  Errors: NULL pointer -> BI8_ERR_NULL; a limit
+ * broken -> BI8_ERR_SHAPE; a pointer not 4-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renormalize,
+                            int32_t *topk_ids, float *topk_weights, int32_t *sorted_token,
+                            int32_t *expert_offsets, int32_t *row_of, void *stream);
+
+/*
+ * blockint8_quant_act on gathered rows: output row r quantises row rows[r]
+ * of x (the dispatch of the tokens to their expert rows; quantising per
+ * token and gathering give the same codes, so this is exact).
+ *
+ *   x     bf16 [T, ldx]   rows int32 [R] on the device, values in [0, T)
+ *                          (an index outside reads as an all-zero row)
+ *   xq    int8 [R, K]      xs fp32 [R, ceil(K/128)]
+ *
+ * Errors: as blockint8_quant_act; NULL rows -> BI8_ERR_NULL; T < 0 ->
+ * BI8_ERR_SHAPE.
+ */
+int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, const int32_t *rows,
+                                   int64_t R, int64_t K, int32_t block_k, int8_t *xq, float *xs,
+                                   void *stream);
+
+/*
+ * Gate/up activation fused with the quantisation of its result, for the w2
+ * GEMM.  h (the w13 output) holds gate in columns [0, I) and up in [I, 2I):
+ *
+ *   a[r, i] = bf16( silu(gate) * up ),  silu(z) = z / (1 + exp(-z))  (fp32)
+ *   aq, as  = blockint8_quant_act(a)   (bit for bit)
+ *
+ *   h   bf16 [R, 2I] (16-byte aligned)   aq int8 [R, I]   as fp32 [R, ceil(I/128)]
+ *   a   bf16 [R, I]  optional copy of the activation (NULL: not written)
+ *
+ * Errors: NULL h/aq/as (R > 0) -> BI8_ERR_NULL; R < 0, I <= 0 -> BI8_ERR_SHAPE;
+ * block_k != 128 -> BI8_ERR_BLOCK; I % 16, h/aq/a not 16-byte aligned, as not
+ * 4-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int32_t block_k, int8_t *aq,
+                                 float *as, uint16_t *a, void *stream);
+
+/*
+ * Weighted combine: out[t, :] = bf16( sum_s w[t, s] * y2[row_of[t, s], :] ),
+ * summed in fp32 in slot order.
+ *
+ *   y2  bf16 [R, H]   row_of int32 [T, k]   topk_weights fp32 [T, k]
+ *   out bf16 [T, H]   (row_of entries outside [0, R) contribute nothing)
+ *
+ * Errors: NULL pointer (T > 0) -> BI8_ERR_NULL; T < 0, R < 0, H <= 0, k < 1
+ * -> BI8_ERR_SHAPE; H % 8, y2/out not 16-byte aligned, row_of / weights not
+ * 4-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_of,
+                              const float *topk_weights, int64_t T, int32_t k, int64_t H,
+                              uint16_t *out, void *stream);
+
 /*
  * Kernel variants.  blockint8_gemm and blockint8_moe_gemm choose a kernel by
  * shape; the *_variant entry points run a named one instead, with the same

@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
                           "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm",
-                          "blockint8_linear", "blockint8_gemm_select", "blockint8_moe_gemm_select",
+                          "blockint8_linear", "blockint8_moe_route", "blockint8_quant_act_gather",
+                          "blockint8_silu_mul_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
                           "blockint8_gemm_variant", "blockint8_moe_gemm_variant"}
     for name in names:
         assert hasattr(lib, name), name
@@ -220,3 +221,66 @@ def test_linear_rejects(lib, kw, status):
 
 def test_linear_empty_is_noop(lib):
     assert linear(lib, M=0, x=None, w=None, ws=None, y=None, xq=None, xs=None) == OK
+
+
+def route(lib, logits=P16, T=16, E=8, k=2, ids=P16, w=P16, st=P16, off=P16, ro=P16):
+    return lib.blockint8_moe_route(logits, T, E, k, 0, ids, w, st, off, ro, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=None), NULL), (dict(ids=None), NULL), (dict(off=None), NULL), (dict(ro=None), NULL),
+    (dict(E=0), SHAPE), (dict(E=1025), SHAPE), (dict(k=0), SHAPE), (dict(k=9, E=16), SHAPE),
+    (dict(k=3, E=2), SHAPE), (dict(T=-1), SHAPE),
+    (dict(logits=P16 + 2), ALIGN), (dict(off=P16 + 1), ALIGN), (dict(w=P16 + 3), ALIGN),
+])
+def test_moe_route_rejects(lib, kw, status):
+    assert route(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_moe_route")
+
+
+def gather(lib, x=P16, T=8, ldx=256, rows=P16, R=4, K=256, bk=128, xq=P16, xs=P16):
+    return lib.blockint8_quant_act_gather(x, T, ldx, rows, R, K, bk, xq, xs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=None), NULL), (dict(x=None), NULL), (dict(xq=None), NULL),
+    (dict(R=-1), SHAPE), (dict(T=-1), SHAPE), (dict(K=0), SHAPE), (dict(ldx=128), SHAPE),
+    (dict(bk=64), BLOCK), (dict(K=200, ldx=200), ALIGN), (dict(rows=P16 + 2), ALIGN), (dict(x=P16 + 8), ALIGN),
+])
+def test_quant_act_gather_rejects(lib, kw, status):
+    assert gather(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_quant_act_gather")
+
+
+def silu(lib, h=P16, R=4, I=256, bk=128, aq=P16, as_=P16, a=None):
+    return lib.blockint8_silu_mul_quant(h, R, I, bk, aq, as_, a, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), NULL), (dict(aq=None), NULL), (dict(as_=None), NULL),
+    (dict(R=-1), SHAPE), (dict(I=0), SHAPE), (dict(bk=256), BLOCK),
+    (dict(I=40), ALIGN), (dict(h=P16 + 8), ALIGN), (dict(a=P16 + 8), ALIGN), (dict(as_=P16 + 2), ALIGN),
+])
+def test_silu_mul_quant_rejects(lib, kw, status):
+    assert silu(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_silu_mul_quant")
+
+
+def combine(lib, y2=P16, R=8, ro=P16, w=P16, T=4, k=2, H=64, out=P16):
+    return lib.blockint8_moe_combine(y2, R, ro, w, T, k, H, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(y2=None), NULL), (dict(ro=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL),
+    (dict(T=-1), SHAPE), (dict(R=-1), SHAPE), (dict(H=0), SHAPE), (dict(k=0), SHAPE),
+    (dict(H=60), ALIGN), (dict(y2=P16 + 8), ALIGN), (dict(out=P16 + 4), ALIGN), (dict(ro=P16 + 1), ALIGN),
+])
+def test_moe_combine_rejects(lib, kw, status):
+    assert combine(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_moe_combine")
+
+
+def test_moe_steps_empty_are_noops(lib):
+    assert gather(lib, R=0, x=None, rows=None, xq=None, xs=None) == OK
+    assert silu(lib, R=0, h=None, aq=None, as_=None) == OK
+    assert combine(lib, T=0, y2=None, ro=None, w=None, out=None) == OK
