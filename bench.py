@@ -97,6 +97,7 @@ class Dense:
         self.xs = torch.empty((self.M, KB), dtype=torch.float32, device="cuda")
         self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
         self.ops = 2 * self.M * self.N * self.K
+        self.quant_shape = (self.M, self.K)
         self.dominant = "gemm"
         self.dominant_bytes = gemm_bytes(self.M, self.N, self.K)
         self.dominant_ops = self.ops
@@ -142,7 +143,9 @@ class Dense:
 
 
 class Moe:
-    """quant_act + grouped gemm for w13, then quant_act + grouped gemm for w2."""
+    """The FusedMoE layer on the GPU, one launch per step: route (top-k of the
+    softmax of the router logits, dispatch order), gather + quantise, w13
+    grouped GEMM, SiLU gating + requantise, w2 grouped GEMM, weighted combine."""
 
     def __init__(self, variant=None):
         c = wl.CONFIGS["moe"]
@@ -151,49 +154,76 @@ class Moe:
         T, H, I, E, k = c["T"], c["H"], c["I"], c["E"], c["topk"]
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         rng = wl.rng_for(c["seed"])
-        x = wl.activations(rng, T, H)
-        logits = wl.router_logits(rng, T, E)
-        tok, _, off = wl.dispatch_topk(logits, k)
-        self.R = T * k
-        self.off_np = off
-        self.x_np = x[tok]
+        self.x_np = wl.activations(rng, T, H)
+        self.logits_np = wl.router_logits(rng, T, E)
         self.w13_np = wl.weights(rng, E, 2 * I, H)
         self.ws13_np = wl.weight_scales(rng, E, *bi8.scale_shape(2 * I, H))
         self.w2_np = wl.weights(rng, E, H, I)
         self.ws2_np = wl.weight_scales(rng, E, *bi8.scale_shape(H, I))
-        self.x2_np = wl.activations(rng, self.R, I)
+        self.R = T * k
         self.x = bf16_dev(self.x_np)
-        self.x2 = bf16_dev(self.x2_np)
-        self.off = dev(off)
+        self.logits = dev(self.logits_np)
         self.w13, self.ws13 = dev(self.w13_np), dev(self.ws13_np)
         self.w2, self.ws2 = dev(self.w2_np), dev(self.ws2_np)
         KB1, KB2 = bi8.scale_shape(1, H)[1], bi8.scale_shape(1, I)[1]
-        self.xq1 = torch.empty((self.R, H), dtype=torch.int8, device="cuda")
-        self.xs1 = torch.empty((self.R, KB1), dtype=torch.float32, device="cuda")
-        self.xq2 = torch.empty((self.R, I), dtype=torch.int8, device="cuda")
-        self.xs2 = torch.empty((self.R, KB2), dtype=torch.float32, device="cuda")
-        self.y13 = torch.empty((self.R, 2 * I), dtype=torch.bfloat16, device="cuda")
-        self.y2 = torch.empty((self.R, H), dtype=torch.bfloat16, device="cuda")
+        d = dict(device="cuda")
+        self.ids = torch.empty((T, k), dtype=torch.int32, **d)
+        self.wts = torch.empty((T, k), dtype=torch.float32, **d)
+        self.st = torch.empty((self.R,), dtype=torch.int32, **d)
+        self.off = torch.empty((E + 1,), dtype=torch.int32, **d)
+        self.row_of = torch.empty((T, k), dtype=torch.int32, **d)
+        self.xq1 = torch.empty((self.R, H), dtype=torch.int8, **d)
+        self.xs1 = torch.empty((self.R, KB1), dtype=torch.float32, **d)
+        self.y13 = torch.empty((self.R, 2 * I), dtype=torch.bfloat16, **d)
+        self.xq2 = torch.empty((self.R, I), dtype=torch.int8, **d)
+        self.xs2 = torch.empty((self.R, KB2), dtype=torch.float32, **d)
+        self.y2 = torch.empty((self.R, H), dtype=torch.bfloat16, **d)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, **d)
         self.copies = 1
+        self.quant_shape = (self.R, H)   # the gathered rows
         self.ops = 2 * self.R * (2 * I) * H + 2 * self.R * H * I
         self.dominant = "moe_gemm_w13"
         self.dominant_ops = 2 * self.R * (2 * I) * H
         self.dominant_bytes = (self.R * H + 4 * self.R * KB1 + E * 2 * I * H
                                + 4 * E * bi8.scale_shape(2 * I, H)[0] * KB1 + 2 * self.R * 2 * I)
-        self.workload = ("moe grouped linear T=%d tokens top-%d of E=%d, hidden %d, "
-                         "intermediate %d, block [128,128]" % (T, k, E, H, I))
+        self.workload = ("moe layer T=%d tokens top-%d of E=%d, hidden %d, intermediate %d, "
+                         "block [128,128]" % (T, k, E, H, I))
+        self.route(0)
+        self.quant(0)   # operands for the dominant kernel timed alone
+
+    def route(self, i):
+        bi8.moe_route(self.logits, self.k, out=(self.ids, self.wts, self.st, self.off, self.row_of))
 
     def quant(self, i):
-        bi8.quant_act(self.x, self.xq1, self.xs1)
+        bi8.quant_act_gather(self.x, self.st, self.xq1, self.xs1)
 
     def dominant_launch(self, i):
         bi8.moe_gemm(self.xq1, self.xs1, self.off, self.w13, self.ws13, y=self.y13, variant=self.variant)
 
     def step(self, i):
+        self.route(i)
         self.quant(i)
         self.dominant_launch(i)
-        bi8.quant_act(self.x2, self.xq2, self.xs2)
+        bi8.silu_mul_quant(self.y13, self.xq2, self.xs2)
         bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2, variant=self.variant)
+        bi8.moe_combine(self.y2, self.row_of, self.wts, out=self.out)
+
+    def parts(self):
+        """Each step of the layer on its own: name -> (launch, algorithmic bytes)."""
+        R, H, I, T, k = self.R, self.H, self.I, self.T, self.k
+        KB1, KB2 = bi8.scale_shape(1, H)[1], bi8.scale_shape(1, I)[1]
+        return {
+            "route": (self.route, 4 * T * self.E + 4 * T * k * 4 + 4 * (self.E + 1)),
+            "gather_quant": (self.quant, quant_bytes(R, H)),
+            "moe_gemm_w13": (self.dominant_launch, self.dominant_bytes),
+            "silu_mul_quant": (lambda i: bi8.silu_mul_quant(self.y13, self.xq2, self.xs2),
+                               2 * R * 2 * I + R * I + 4 * R * KB2),
+            "moe_gemm_w2": (lambda i: bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2,
+                                                   variant=self.variant),
+                            R * I + 4 * R * KB2 + self.E * H * I + 2 * R * H),
+            "combine": (lambda i: bi8.moe_combine(self.y2, self.row_of, self.wts, out=self.out),
+                        2 * R * H + 8 * T * k + 2 * T * H),
+        }
 
     def config(self):
         v = (bi8.moe_gemm_select(self.R, 2 * self.I, self.H, self.E) if self.variant is None
@@ -203,20 +233,30 @@ class Moe:
                 "kernel": VARIANT_NAMES[v]}
 
     def cpu_sample(self, budget_s):
+        """Time the oracle's layer (route, quantise, w13 GEMM, SiLU, requantise,
+        w2 GEMM, combine) on a bounded sample of tokens."""
         import oracle
-        e0 = 0
-        a, b = int(self.off_np[e0]), int(self.off_np[e0 + 1])
+        ids, wts = oracle.topk_softmax(self.logits_np, self.k)
+
+        def layer(tokens):
+            n = len(tokens)
+            st, off, row_of = oracle.moe_align(ids[tokens], self.E)
+            xq, xs = oracle.quant_act(self.x_np[tokens][st])
+            h = oracle.moe_gemm(xq, xs, off, self.w13_np, self.ws13_np)
+            aq, as_ = oracle.quant_act(oracle.silu_mul(h))
+            y2 = oracle.moe_gemm(aq, as_, off, self.w2_np, self.ws2_np)
+            oracle.combine(y2, row_of, wts[tokens].astype(np.float32))
+            return n
+
         t0 = time.perf_counter()
-        xq, xs = oracle.quant_act(self.x_np[a:a + 1])
-        oracle.gemm(xq, xs, self.w13_np[e0], self.ws13_np[e0])
-        t_row = max(time.perf_counter() - t0, 1e-4)
-        rows = int(max(1, min(b - a, budget_s / t_row)))
+        layer(np.arange(1))
+        t_tok = max(time.perf_counter() - t0, 1e-4)
+        n = int(max(1, min(self.T, budget_s / t_tok)))
         t0 = time.perf_counter()
-        xq, xs = oracle.quant_act(self.x_np[a:a + rows])
-        oracle.gemm(xq, xs, self.w13_np[e0], self.ws13_np[e0])
+        layer(np.arange(n))
         dt = time.perf_counter() - t0
-        ops = 2.0 * rows * 2 * self.I * self.H
-        return ops / dt / 1e12, "%d rows of expert 0, w13 projection, quant+GEMM, %.1f s" % (rows, dt)
+        ops = 2.0 * n * self.k * (2 * self.I * self.H + self.H * self.I)
+        return ops / dt / 1e12, "first %d of %d tokens through the whole layer, %.1f s" % (n, self.T, dt)
 
 
 def make_workload(name, copies=None, variant=None):
@@ -330,6 +370,13 @@ def main():
     _, ev_q = timed(w.quant, args.steps, use_graph)
     t_q = ev_q / args.steps
 
+    parts = None
+    if hasattr(w, "parts"):
+        parts = {}
+        for name, (fn, nbytes) in w.parts().items():
+            _, ev_p = timed(fn, args.steps, use_graph)
+            t_p = ev_p / args.steps
+            parts[name] = {"avg_launch_us": round(t_p * 1e6, 3), "GB/s": round(nbytes / t_p / 1e9, 1)}
     value = w.ops / (wall / args.steps) / 1e12
     hbm_bound = w.dominant_ops / (INT8_PEAK_TOPS * 1e12) < w.dominant_bytes / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
@@ -352,7 +399,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic", "config": w.config(), "roofline": roof,
         "quant_act": {"avg_launch_us": round(t_q * 1e6, 3),
-                      "GB/s": round(quant_bytes(*(w.x.shape)) / t_q / 1e9, 1)},
+                      "GB/s": round(quant_bytes(*w.quant_shape) / t_q / 1e9, 1)},
+        "steps_alone": parts,
         "event_ms_per_step": round(ev / args.steps * 1e3, 5),
         "timing": "hip graph of %d steps, one replay" % args.steps if use_graph else "eager launches",
     }

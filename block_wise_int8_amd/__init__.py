@@ -273,19 +273,28 @@ def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tenso
 
 # ----------------------------------------------------------------- MoE --
 
-def moe_route(logits: torch.Tensor, k: int, renormalize: bool = False):
+def moe_route(logits: torch.Tensor, k: int, renormalize: bool = False, out=None):
     """Top-k routing and dispatch order for fp32 router logits [T, E].
 
     Returns ``(topk_ids int32 [T, k], topk_weights fp32 [T, k], sorted_token
-    int32 [T*k], expert_offsets int32 [E+1], row_of int32 [T, k])``."""
+    int32 [T*k], expert_offsets int32 [E+1], row_of int32 [T, k])``, written
+    into ``out`` (a tuple of those five tensors) when given."""
     _need(logits, "logits", torch.float32, 2)
     T, E = logits.shape
     dev = logits.device
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    st = torch.empty((T * k,), dtype=torch.int32, device=dev)
-    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T * k,), dtype=torch.int32, device=dev),
+               torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev))
+    ids, w, st, off, row_of = out
+    for t, name, dt, shape in ((ids, "topk_ids", torch.int32, (T, k)), (w, "topk_weights", torch.float32, (T, k)),
+                               (st, "sorted_token", torch.int32, (T * k,)), (off, "expert_offsets", torch.int32, (E + 1,)),
+                               (row_of, "row_of", torch.int32, (T, k))):
+        _need(t, name, dt, len(shape))
+        if tuple(t.shape) != shape:
+            raise ValueError("%s must have shape %s" % (name, shape))
     _check(load().blockint8_moe_route(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
                                       _ptr(st), _ptr(off), _ptr(row_of), _stream_handle(dev)))
     return ids, w, st, off, row_of

@@ -68,22 +68,3 @@ def weight_scales(rng, *shape) -> np.ndarray:
 
 def router_logits(rng, T: int, E: int) -> np.ndarray:
     return rng.standard_normal((T, E), dtype=np.float32)
-
-
-def dispatch_topk(logits: np.ndarray, k: int):
-    """Dispatch each token to its k largest-logit experts (ties: lower index).
-
-    Returns (row_token int64 [T*k], row_slot int64 [T*k], offsets int32 [E+1]):
-    the dispatched rows in (expert, token, slot) order and each expert's row
-    segment [offsets[e], offsets[e+1]).
-    """
-    T, E = logits.shape
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]       # [T, k]
-    experts = order.reshape(-1)
-    tokens = np.repeat(np.arange(T), k)
-    slots = np.tile(np.arange(k), T)
-    perm = np.lexsort((slots, tokens, experts))
-    counts = np.bincount(experts, minlength=E)
-    offsets = np.zeros(E + 1, np.int32)
-    offsets[1:] = np.cumsum(counts)
-    return tokens[perm], slots[perm], offsets
