@@ -52,12 +52,13 @@ def _load():
     lib.oracle_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64]
     lib.oracle_gemm_f64.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64]
     lib.oracle_moe_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64]
+    lib.oracle_quant_weight.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp]
     lib.oracle_topk_softmax.argtypes = [vp, i64, i64, i64, ctypes.c_int, vp, vp]
     lib.oracle_moe_align.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     lib.oracle_silu_mul.argtypes = [vp, i64, i64, vp]
     lib.oracle_combine.argtypes = [vp, i64, vp, vp, i64, i64, i64, vp]
     for f in ("oracle_scale_shape", "oracle_quant_act", "oracle_gemm", "oracle_gemm_f64",
-              "oracle_moe_gemm", "oracle_topk_softmax", "oracle_moe_align", "oracle_silu_mul",
+              "oracle_moe_gemm", "oracle_quant_weight", "oracle_topk_softmax", "oracle_moe_align", "oracle_silu_mul",
               "oracle_combine"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
@@ -151,6 +152,22 @@ def moe_gemm(xq, xs, offsets, w, ws, block=(128, 128)) -> np.ndarray:
     _check(_load().oracle_moe_gemm(_ptr(xq), _ptr(xs), _ptr(off), _ptr(w), _ptr(ws), _ptr(y),
                                    R, N, K, E, block[0], block[1]), "moe_gemm")
     return y
+
+
+def quant_weight(w_bf16, block=(128, 128), K: int | None = None):
+    """Block quantisation of a bf16 weight [N, ldw] (``K`` columns, default ldw).
+
+    Returns (wq int8 [N, K], ws float32 [ceil(N/bn), ceil(K/bk)])."""
+    w = _c(w_bf16, np.uint16)
+    N, ldw = w.shape
+    K = ldw if K is None else K
+    NB = (N + block[0] - 1) // block[0] if N > 0 else 0
+    KB = (K + block[1] - 1) // block[1] if K > 0 else 0
+    wq = np.zeros((N, K), np.int8)
+    ws = np.zeros((NB, KB), np.float32)
+    _check(_load().oracle_quant_weight(_ptr(w), N, K, ldw, block[0], block[1], _ptr(wq), _ptr(ws)),
+           "quant_weight")
+    return wq, ws
 
 
 # ------------------------------------------------------------ MoE steps --

@@ -346,3 +346,48 @@ int oracle_combine(const uint16_t *y2, int64_t R, const int32_t *row_of, const f
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Offline weight quantisation                                          */
+/* ------------------------------------------------------------------ */
+
+/* [BW8] §1: the method loads only int8-serialised weights; §2: one fp32
+ * scale per (block_n x block_k) block of the [N, K] weight, scale tensor
+ * [ceil(N/bn), ceil(K/bk)]; design rationale item 3: the scale multiplies
+ * on dequantisation.  Producing such a checkpoint from a bf16 weight uses the
+ * same symmetric encoding as the activations, per 2-D block:
+ *   s = amax over the block / 127 (binary32),
+ *   q = 0 if s == 0, else clamp(rne(w / s), -127, 127).
+ * The blocks at the N and K ends are ragged.  w is bf16 bits [N, ldw]. */
+int oracle_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t ldw, int64_t block_n,
+                        int64_t block_k, int8_t *wq, float *ws)
+{
+    if (N < 0 || K < 0 || ldw < K || block_n <= 0 || block_k <= 0) return -1;
+    if (N > 0 && K > 0 && (!w || !wq || !ws)) return -1;
+    const int64_t NB = (N + block_n - 1) / block_n, KB = (K + block_k - 1) / block_k;
+    for (int64_t bn = 0; bn < NB; ++bn)
+        for (int64_t bk = 0; bk < KB; ++bk) {
+            const int64_t n0 = bn * block_n, n1 = (n0 + block_n < N) ? n0 + block_n : N;
+            const int64_t k0 = bk * block_k, k1 = (k0 + block_k < K) ? k0 + block_k : K;
+            float amax = 0.0f;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t k = k0; k < k1; ++k) {
+                    const float v = bf16_bits_to_f32(w[n * ldw + k]);
+                    if (!isfinite(v)) return -2;
+                    if (fabsf(v) > amax) amax = fabsf(v);
+                }
+            const float s = amax / 127.0f;
+            ws[bn * KB + bk] = s;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t k = k0; k < k1; ++k) {
+                    float q = 0.0f;
+                    if (s != 0.0f) {
+                        q = rintf(bf16_bits_to_f32(w[n * ldw + k]) / s);
+                        if (q > 127.0f) q = 127.0f;
+                        if (q < -127.0f) q = -127.0f;
+                    }
+                    wq[n * K + k] = (int8_t)q;
+                }
+        }
+    return 0;
+}

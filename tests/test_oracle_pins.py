@@ -541,3 +541,64 @@ def test_combine_special_cases():
     # doubling the weights doubles the output exactly
     assert np.array_equal(bits_to_f32(oracle.combine(y2, row_of, 2 * w2)),
                           2 * bits_to_f32(oracle.combine(y2, row_of, w2)))
+
+
+# ------------------------------------------------ offline weight quantiser --
+
+def test_quant_weight_block_rows_equal_activation_quantiser():
+    """block_n = 1 is the per-(row, K-group) encoding of the activations."""
+    rng = np.random.default_rng(31)
+    w = wl.activations(rng, 37, 300, 0.02)
+    wq, ws = oracle.quant_weight(w, block=(1, 128))
+    xq, xs = oracle.quant_act(w)
+    assert np.array_equal(wq, xq) and np.array_equal(ws, xs)
+
+
+def test_quant_weight_scale_shape_and_ties():
+    w = np.zeros((4096, 4096), np.uint16)
+    wq, ws = oracle.quant_weight(w)
+    assert ws.shape == (32, 32) and not ws.any() and not wq.any()          # the pages' worked example
+    blk = np.zeros((128, 128), np.float32)
+    blk[5, 7] = 127.0                                                      # s = 1 exactly
+    blk[0, :5] = [0.5, 1.5, 2.5, -2.5, 126.5]
+    blk[100, 3] = -127.0
+    wq, ws = oracle.quant_weight(bf16_bits(blk))
+    assert ws[0, 0] == 1.0
+    assert wq[0, :5].tolist() == [0, 2, 2, -2, 126]                         # round half to even
+    assert wq[5, 7] == 127 and wq[100, 3] == -127
+
+
+def test_quant_weight_invariants_and_ragged_padding():
+    rng = np.random.default_rng(32)
+    N, K = 300, 400
+    w = wl.activations(rng, N, K)
+    wq, ws = oracle.quant_weight(w)
+    assert ws.shape == (3, 4) and np.abs(wq.astype(int)).max() <= 127
+    wf = bits_to_f32(w).astype(np.float64)
+    s = np.repeat(np.repeat(ws, 128, 0), 128, 1)[:N, :K].astype(np.float64)
+    assert np.all(np.abs(wf - wq * s) <= s * (0.5 + 2.0 ** -16))
+    for bn in range(3):                                                   # each block's max hits 127
+        for bk in range(4):
+            blk = np.abs(wq[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128].astype(int))
+            assert blk.max() == 127
+    # zero padding to whole blocks changes nothing
+    wp = np.zeros((384, 512), np.uint16)
+    wp[:N, :K] = w
+    wqp, wsp = oracle.quant_weight(wp)
+    assert np.array_equal(wqp[:N, :K], wq) and np.array_equal(wsp, ws)
+
+
+def test_quant_weight_transpose_swaps_blocks():
+    rng = np.random.default_rng(33)
+    w = wl.activations(rng, 200, 136)
+    wq, ws = oracle.quant_weight(w, block=(64, 32))
+    wqt, wst = oracle.quant_weight(np.ascontiguousarray(w.T), block=(32, 64))
+    assert np.array_equal(wqt, wq.T) and np.array_equal(wst, ws.T)
+
+
+def test_quant_weight_row_stride():
+    rng = np.random.default_rng(34)
+    w = wl.activations(rng, 50, 272)
+    wq, ws = oracle.quant_weight(w, K=256)          # ldw = 272
+    wq2, ws2 = oracle.quant_weight(np.ascontiguousarray(w[:, :256]))
+    assert np.array_equal(wq, wq2) and np.array_equal(ws, ws2)
