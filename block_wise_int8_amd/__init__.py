@@ -28,7 +28,7 @@ import torch
 
 __all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "moe_gemm",
            "linear", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
-           "silu_mul_quant", "moe_combine", "moe_layer", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
+           "silu_mul_quant", "moe_combine", "moe_layer", "quant_weight", "check_tp_partition", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
            "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
 
 BLOCK = 128
@@ -79,11 +79,14 @@ def load() -> ctypes.CDLL:
     lib.blockint8_moe_gemm_variant.argtypes = [i32] + lib.blockint8_moe_gemm.argtypes
     lib.blockint8_linear.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
     lib.blockint8_moe_route.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.blockint8_quant_weight.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp]
+    lib.blockint8_check_tp_partition.argtypes = [i64, i64, vp, i32, i32, i32, i32]
     lib.blockint8_quant_act_gather.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, vp]
     lib.blockint8_silu_mul_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     lib.blockint8_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, vp]
     for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_linear",
-              "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_silu_mul_quant",
+              "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_quant_weight",
+              "blockint8_check_tp_partition", "blockint8_silu_mul_quant",
               "blockint8_moe_combine", "blockint8_gemm_select",
               "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant"):
         getattr(lib, f).restype = i32
@@ -375,3 +378,32 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, ws13: to
     aq, as_ = silu_mul_quant(h)
     y2 = moe_gemm(aq, as_, off, w2, ws2, variant=variant)
     return moe_combine(y2, row_of, w)
+
+
+# ------------------------------------------------------- weight preparation --
+
+def quant_weight(w: torch.Tensor, block=(BLOCK, BLOCK)):
+    """Block quantisation of a bf16 weight [N, K] -> (int8 [N, K], fp32 [ceil(N/128), ceil(K/128)])."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 2 or w.dtype != torch.bfloat16:
+        raise TypeError("w must be a 2-D bfloat16 tensor")
+    if w.device.type != "cuda":
+        raise ValueError("w must be on a HIP device; there is no CPU path")
+    if w.stride(1) != 1:
+        raise ValueError("w rows must be contiguous (stride(1) == 1)")
+    N, K = w.shape
+    NB, KB = scale_shape(N, K, *block)
+    wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    ws = torch.empty((NB, KB), dtype=torch.float32, device=w.device)
+    ldw = w.stride(0) if N > 1 else K
+    _check(load().blockint8_quant_weight(_ptr(w), N, K, ldw, block[0], block[1], _ptr(wq), _ptr(ws),
+                                         _stream_handle(w.device)))
+    return wq, ws
+
+
+def check_tp_partition(input_size: int, input_size_per_partition: int, output_partition_sizes,
+                       tp_size: int, block=(BLOCK, BLOCK)) -> None:
+    """Raise BlockInt8Error unless the tensor-parallel partition boundaries
+    fall on block boundaries (host only)."""
+    sizes = (ctypes.c_int64 * len(output_partition_sizes))(*[int(v) for v in output_partition_sizes])
+    _check(load().blockint8_check_tp_partition(int(input_size), int(input_size_per_partition), sizes,
+                                               len(output_partition_sizes), int(tp_size), block[0], block[1]))

@@ -205,6 +205,45 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
                                       block_n, block_k, stream);
 }
 
+int32_t blockint8_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t ldw, int32_t block_n,
+                               int32_t block_k, int8_t *wq, float *ws, void *stream) {
+    static const char fn[] = "blockint8_quant_weight";
+    if (N < 0 || N > 65535ll * 128) return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
+    int32_t s = check_k(fn, K);
+    if (s) return s;
+    if (ldw < K) return fail(BI8_ERR_SHAPE, "%s: ldw = %lld < K = %lld", fn, (long long)ldw, (long long)K);
+    if ((s = check_block(fn, block_n, block_k))) return s;
+    if (N == 0) return ok();
+    if (!w || !wq || !ws) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (ldw % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldw = %lld must be a multiple of 8", fn, (long long)ldw);
+    if (!aligned(w, 16) || !aligned(wq, 16)) return fail(BI8_ERR_ALIGN, "%s: w and wq must be 16-byte aligned", fn);
+    if (!aligned(ws, 4)) return fail(BI8_ERR_ALIGN, "%s: ws must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_quant_weight(w, N, K, ldw, wq, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t blockint8_check_tp_partition(int64_t input_size, int64_t input_size_per_partition,
+                                     const int64_t *output_partition_sizes, int32_t n_out,
+                                     int32_t tp_size, int32_t block_n, int32_t block_k) {
+    static const char fn[] = "blockint8_check_tp_partition";
+    if (block_n <= 0 || block_k <= 0 || tp_size <= 0 || input_size <= 0 || input_size_per_partition <= 0 ||
+        n_out < 0)
+        return fail(BI8_ERR_SHAPE, "%s: sizes, tp_size and block dimensions must be positive", fn);
+    if (n_out > 0 && !output_partition_sizes) return fail(BI8_ERR_NULL, "%s: NULL output_partition_sizes", fn);
+    if (tp_size > 1 && input_size / input_size_per_partition == tp_size &&
+        input_size_per_partition % block_k != 0)
+        return fail(BI8_ERR_BLOCK, "%s: input size per partition %lld is not a multiple of block_k = %d",
+                    fn, (long long)input_size_per_partition, block_k);
+    for (int32_t i = 0; i < n_out; ++i) {
+        if (output_partition_sizes[i] <= 0)
+            return fail(BI8_ERR_SHAPE, "%s: output partition %d has size %lld", fn, i,
+                        (long long)output_partition_sizes[i]);
+        if (output_partition_sizes[i] % block_n != 0)
+            return fail(BI8_ERR_BLOCK, "%s: output partition size %lld is not a multiple of block_n = %d", fn,
+                        (long long)output_partition_sizes[i], block_n);
+    }
+    return ok();
+}
+
 int32_t blockint8_moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renormalize,
                             int32_t *topk_ids, float *topk_weights, int32_t *sorted_token,
                             int32_t *expert_offsets, int32_t *row_of, void *stream) {

@@ -21,6 +21,10 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t ldx, const int32_t *rows,
                                    int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream);
 
+// Offline block quantisation of a bf16 weight (128 x 128 blocks).
+hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t ldw, int8_t *wq, float *ws,
+                               hipStream_t stream);
+
 // MoE steps around the grouped GEMM (E <= 1024, k <= 8).
 hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renorm,
                             int32_t *ids, float *weights, int32_t *sorted_token, int32_t *offsets,

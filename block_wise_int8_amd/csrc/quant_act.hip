@@ -103,3 +103,82 @@ hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t 
 }
 
 }  // namespace bi8
+
+// Offline block quantisation of a bf16 weight [N, K] (row stride ldw):
+// one scale per 128 x 128 block, s = amax / 127, codes clamp(rne(w / s)).
+// Page "[SGLang] Block-wise INT8", sections 1 and 2 (int8-serialised weights
+// with one fp32 scale per block) and design rationale item 3.
+//
+// One workgroup of 256 threads per block: thread t covers row t / 2 of the
+// block and its half t % 2 (64 entries, eight 16-byte loads).  The block max
+// is reduced over the wave with cross-lane moves, then over the four waves
+// through LDS.  Rows past N and 8-entry pieces past K (K % 16 == 0) read as
+// zero and are not written.
+namespace bi8 {
+
+namespace {
+
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t *__restrict__ w, int64_t N, int64_t K,
+                                                           int64_t ldw, int8_t *__restrict__ wq,
+                                                           float *__restrict__ ws, int64_t KB) {
+    __shared__ float wmax[4];
+    const int t = threadIdx.x;
+    const int64_t bn = blockIdx.y, bk = blockIdx.x;
+    const int64_t n = bn * kBlock + (t >> 1);
+    const int64_t k0 = bk * kBlock + (t & 1) * 64;
+    const bool row_ok = n < N;
+    float f[64];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok && k0 + 8 * c < K) v = *reinterpret_cast<const u32x4 *>(w + n * ldw + k0 + 8 * c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[8 * c + 2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
+            f[8 * c + 2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = wave_max64(amax);
+    if ((t & 63) == 0) wmax[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = amax / 127.0f;
+    if (t == 0) ws[bn * KB + bk] = s;
+    if (!row_ok) return;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        if (k0 + 8 * c >= K) break;
+        uint32_t lo = 0u, hi = 0u;
+        if (s != 0.0f) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= ((uint32_t)quant_one(f[8 * c + j], s) & 0xFFu) << (8 * j);
+                hi |= ((uint32_t)quant_one(f[8 * c + 4 + j], s) & 0xFFu) << (8 * j);
+            }
+        }
+        *reinterpret_cast<uint2 *>(wq + n * K + k0 + 8 * c) = make_uint2(lo, hi);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t ldw, int8_t *wq, float *ws,
+                               hipStream_t stream) {
+    const int64_t NB = (N + kBlock - 1) / kBlock, KB = (K + kBlock - 1) / kBlock;
+    if (NB == 0 || KB == 0) return hipSuccess;
+    if (NB > 65535 || KB > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)KB, (unsigned)NB), dim3(256), 0, stream, w, N, K, ldw,
+                       wq, ws, KB);
+    return hipGetLastError();
+}
+
+}  // namespace bi8

@@ -160,6 +160,39 @@ int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
                          int32_t block_n, int32_t block_k, int8_t *xq_workspace,
                          float *xs_workspace, void *stream);
 
+/*
+ * Offline block quantisation of a bf16 weight into the int8 + fp32 block
+ * scale form that blockint8_gemm consumes (section 1 of the page: only
+ * int8-serialised weights are loaded; section 2: one fp32 scale per
+ * (block_n x block_k) block, scale tensor [ceil(N/bn), ceil(K/bk)]).  Per
+ * block: s = amax / 127, q = clamp(rne(w / s), -127, 127), 0 when s == 0 --
+ * the same encoding as the activations, per 2-D block.
+ *
+ *   w   bf16 [N, ldw]  (ldw >= K, ldw % 8 == 0, 16-byte aligned)
+ *   wq  int8 [N, K]    (16-byte aligned)   ws fp32 [ceil(N/128), ceil(K/128)]
+ *
+ * Limits: N <= 65535 * 128.  Errors: NULL pointer (N > 0) -> BI8_ERR_NULL;
+ * N < 0, K <= 0, ldw < K, N too large -> BI8_ERR_SHAPE; block != [128, 128]
+ * -> BI8_ERR_BLOCK; K % 16, ldw % 8 or alignment -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t ldw, int32_t block_n,
+                               int32_t block_k, int8_t *wq, float *ws, void *stream);
+
+/*
+ * Tensor-parallel partition check (section 3 of the page): block
+ * quantisation needs the partition boundaries on block boundaries.
+ *   row parallel:    when tp_size > 1 and input_size / input_size_per_partition
+ *                    == tp_size, input_size_per_partition % block_k == 0;
+ *   column parallel: every output_partition_sizes[i] % block_n == 0.
+ * Host only (no device pointer, no launch).  Returns BI8_OK, or
+ * BI8_ERR_BLOCK with the offending size in blockint8_last_error();
+ * BI8_ERR_NULL / BI8_ERR_SHAPE for a NULL array with n_out > 0 or a
+ * non-positive size.
+ */
+int32_t blockint8_check_tp_partition(int64_t input_size, int64_t input_size_per_partition,
+                                     const int64_t *output_partition_sizes, int32_t n_out,
+                                     int32_t tp_size, int32_t block_n, int32_t block_k);
+
 /* ---------------------------------------------------------------------
  * The MoE steps on either side of the grouped GEMM (section 6 of the page:
  * the fused-MoE runner routes the tokens, runs the per-expert int8 GEMMs and

@@ -39,6 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
                           "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm",
                           "blockint8_linear", "blockint8_moe_route", "blockint8_quant_act_gather",
+                          "blockint8_quant_weight", "blockint8_check_tp_partition",
                           "blockint8_silu_mul_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
                           "blockint8_gemm_variant", "blockint8_moe_gemm_variant"}
     for name in names:
@@ -284,3 +285,51 @@ def test_moe_steps_empty_are_noops(lib):
     assert gather(lib, R=0, x=None, rows=None, xq=None, xs=None) == OK
     assert silu(lib, R=0, h=None, aq=None, as_=None) == OK
     assert combine(lib, T=0, y2=None, ro=None, w=None, out=None) == OK
+
+
+def tp_cases():
+    path = os.path.join(ROOT, "tests", "golden", "tp_partition_cases.txt")
+    for line in open(path):
+        line = line.split("#")[0].split()
+        if line:
+            yield ([int(v) for v in line[:5]], [int(v) for v in line[5].split(",")], line[6])
+
+
+@pytest.mark.parametrize("case", list(tp_cases()))
+def test_check_tp_partition_follows_the_rule(lib, case):
+    (ins, per, tp, bn, bk), outs, expected = case
+    if expected == "ok":
+        bi8.check_tp_partition(ins, per, outs, tp, block=(bn, bk))
+        assert lib.blockint8_last_error().decode() == ""
+    else:
+        with pytest.raises(bi8.BlockInt8Error, match="BI8_ERR_BLOCK"):
+            bi8.check_tp_partition(ins, per, outs, tp, block=(bn, bk))
+
+
+def test_check_tp_partition_rejects_bad_arguments(lib):
+    assert lib.blockint8_check_tp_partition(4096, 4096, None, 1, 1, 128, 128) == NULL
+    assert lib.blockint8_check_tp_partition(0, 4096, None, 0, 1, 128, 128) == SHAPE
+    assert lib.blockint8_check_tp_partition(4096, 4096, None, 0, 0, 128, 128) == SHAPE
+    assert lib.blockint8_check_tp_partition(4096, 4096, None, 0, 1, 0, 128) == SHAPE
+    with pytest.raises(bi8.BlockInt8Error, match="BI8_ERR_SHAPE"):
+        bi8.check_tp_partition(4096, 4096, [128, 0], 1)
+
+
+def qweight(lib, w=P16, N=256, K=256, ldw=256, bn=128, bk=128, wq=P16, ws=P16):
+    return lib.blockint8_quant_weight(w, N, K, ldw, bn, bk, wq, ws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), NULL), (dict(wq=None), NULL), (dict(ws=None), NULL),
+    (dict(N=-1), SHAPE), (dict(N=65536 * 128), SHAPE), (dict(K=0), SHAPE), (dict(ldw=128), SHAPE),
+    (dict(bn=64), BLOCK), (dict(bk=256), BLOCK),
+    (dict(K=200, ldw=200), ALIGN), (dict(ldw=260), ALIGN), (dict(w=P16 + 8), ALIGN), (dict(wq=P16 + 4), ALIGN),
+    (dict(ws=P16 + 2), ALIGN),
+])
+def test_quant_weight_rejects(lib, kw, status):
+    assert qweight(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_quant_weight")
+
+
+def test_quant_weight_empty_is_noop(lib):
+    assert qweight(lib, N=0, w=None, wq=None, ws=None) == OK
