@@ -59,9 +59,9 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def gemm_bytes(M, N, K):
+def gemm_bytes(M, N, K, block=(128, 128)):
     """Algorithmic HBM bytes of one GEMM launch: xq + xs + w + ws + y."""
-    NB, KB = bi8.scale_shape(N, K)
+    NB, KB = bi8.scale_shape(N, K, *block)
     return M * K + 4 * M * KB + N * K + 4 * NB * KB + 2 * M * N
 
 
@@ -78,40 +78,44 @@ def n_copies(weight_bytes, override=None):
 class Dense:
     """quant_act + gemm on one [M, K] x [N, K] linear."""
 
-    def __init__(self, name, copies=None, variant=None):
+    def __init__(self, name, copies=None, variant=None, per_channel=False):
         c = wl.CONFIGS[name]
         self.name = name
         self.variant = variant
+        self.per_channel = per_channel
         self.M, self.N, self.K = c["M"], c["N"], c["K"]
         rng = wl.rng_for(c["seed"])
         self.x_np = wl.activations(rng, self.M, self.K, c.get("outlier_frac", 0.0))
         self.w_np = wl.weights(rng, self.N, self.K)
-        self.ws_np = wl.weight_scales(rng, *bi8.scale_shape(self.N, self.K))
+        # per-channel: blocks of 1 x K (one scale per weight row and per token)
+        self.block = (1, self.K) if per_channel else (128, 128)
+        self.ws_np = wl.weight_scales(rng, *bi8.scale_shape(self.N, self.K, *self.block))
         self.x = bf16_dev(self.x_np)
         w, ws = dev(self.w_np), dev(self.ws_np)
         self.copies = n_copies(self.N * self.K, copies)
         self.w = [w] + [w.clone() for _ in range(self.copies - 1)]
         self.ws = [ws] + [ws.clone() for _ in range(self.copies - 1)]
-        KB = bi8.scale_shape(self.N, self.K)[1]
+        KB = bi8.scale_shape(self.N, self.K, *self.block)[1]
         self.xq = torch.empty((self.M, self.K), dtype=torch.int8, device="cuda")
         self.xs = torch.empty((self.M, KB), dtype=torch.float32, device="cuda")
         self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
         self.ops = 2 * self.M * self.N * self.K
         self.quant_shape = (self.M, self.K)
-        self.dominant = "gemm"
-        self.dominant_bytes = gemm_bytes(self.M, self.N, self.K)
+        self.dominant = "gemm_per_channel" if per_channel else "gemm"
+        self.dominant_bytes = gemm_bytes(self.M, self.N, self.K, self.block)
         self.dominant_ops = self.ops
         outl = c.get("outlier_frac", 0.0)
-        self.workload = ("%s linear M=%d K=%d N=%d block [128,128]%s" %
+        self.workload = ("%s linear M=%d K=%d N=%d %s%s" %
                          (name, self.M, self.K, self.N,
+                          "per-channel (blocks 1 x K)" if per_channel else "block [128,128]",
                           ", %g%% outlier channels x%g" % (100 * outl, c["outlier_scale"]) if outl else ""))
 
     def quant(self, i):
-        bi8.quant_act(self.x, self.xq, self.xs)
+        bi8.quant_act(self.x, self.xq, self.xs, block_k=self.block[1])
 
     def dominant_launch(self, i):
         j = i % self.copies
-        bi8.gemm(self.xq, self.xs, self.w[j], self.ws[j], y=self.y, variant=self.variant)
+        bi8.gemm(self.xq, self.xs, self.w[j], self.ws[j], y=self.y, block=self.block, variant=self.variant)
 
     def step(self, i):
         self.quant(i)
@@ -120,22 +124,23 @@ class Dense:
     def config(self):
         v = bi8.gemm_select(self.M, self.N, self.K) if self.variant is None else self.variant
         return {"workload": self.workload, "M": self.M, "K": self.K, "N": self.N,
-                "block": [128, 128], "weight_copies": self.copies, "kernel": VARIANT_NAMES[v]}
+                "block": list(self.block), "weight_copies": self.copies,
+                "kernel": "per-channel" if self.per_channel else VARIANT_NAMES[v]}
 
     def cpu_sample(self, budget_s):
         """Time the oracle (quant + GEMM) on a bounded sample of rows."""
         import oracle
         # one row costs N*K MACs; pick rows to fill roughly the budget
         t0 = time.perf_counter()
-        xq, xs = oracle.quant_act(self.x_np[:1])
-        oracle.gemm(xq, xs, self.w_np, self.ws_np)
+        xq, xs = oracle.quant_act(self.x_np[:1], block_k=self.block[1])
+        oracle.gemm(xq, xs, self.w_np, self.ws_np, block=self.block)
         t_row = max(time.perf_counter() - t0, 1e-4)
         rows = int(max(1, min(self.M, budget_s / t_row)))
         reps = int(max(1, min(50, budget_s / (t_row * rows))))
         t0 = time.perf_counter()
         for _ in range(reps):
-            xq, xs = oracle.quant_act(self.x_np[:rows])
-            oracle.gemm(xq, xs, self.w_np, self.ws_np)
+            xq, xs = oracle.quant_act(self.x_np[:rows], block_k=self.block[1])
+            oracle.gemm(xq, xs, self.w_np, self.ws_np, block=self.block)
         dt = time.perf_counter() - t0
         ops = 2.0 * rows * self.N * self.K * reps
         return ops / dt / 1e12, "%d of %d token rows x all N, quant+GEMM, %d repetition(s), %.1f s" % (
@@ -259,8 +264,10 @@ class Moe:
         return ops / dt / 1e12, "first %d of %d tokens through the whole layer, %.1f s" % (n, self.T, dt)
 
 
-def make_workload(name, copies=None, variant=None):
-    return Moe(variant) if name == "moe" else Dense(name, copies, variant)
+def make_workload(name, copies=None, variant=None, per_channel=False):
+    if name == "moe":
+        return Moe(variant)
+    return Dense(name, copies, variant, per_channel)
 
 
 def capture(fn, steps):
@@ -324,6 +331,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS),
                     help="GEMM kernel (default: the library's shape-based choice)")
+    ap.add_argument("--per-channel", action="store_true",
+                    help="dense workloads in the per-channel form (blocks of 1 x K)")
     ap.add_argument("--copies", type=int, default=None,
                     help="weight copies to rotate over (default: enough to exceed the Infinity Cache)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -352,7 +361,10 @@ def main():
 
     bi8.load()
     log("[bench] setting up workload %s" % args.workload)
-    w = make_workload(args.workload, args.copies, VARIANTS[args.variant])
+    if args.per_channel and args.workload == "moe":
+        print("--per-channel applies to the dense workloads", file=sys.stderr)
+        sys.exit(2)
+    w = make_workload(args.workload, args.copies, VARIANTS[args.variant], args.per_channel)
     use_graph = not args.eager
 
     log("[bench] warmup %d steps" % args.warmup)

@@ -48,6 +48,12 @@ int32_t check_block(const char *fn, int32_t block_n, int32_t block_k) {
     return BI8_OK;
 }
 
+// The per-channel form of the method is the degenerate block (1, K): one
+// scale per weight row and one per token.  Its int32 sums span all of K.
+constexpr int64_t kMaxPerChannelK = 1 << 17;   // 127^2 * 2^17 < 2^31
+
+bool per_channel(int32_t block_n, int32_t block_k, int64_t K) { return block_n == 1 && block_k == K; }
+
 int32_t check_k(const char *fn, int64_t K) {
     if (K <= 0 || K > BI8_MAX_K)
         return fail(BI8_ERR_SHAPE, "%s: K = %lld out of range [1, %d]", fn, (long long)K, BI8_MAX_K);
@@ -61,17 +67,24 @@ int32_t hip_status(const char *fn, hipError_t e) {
     return ok();
 }
 
-// Checks shared by the dense and grouped GEMM.
+// Checks shared by the dense and grouped GEMM (allow_pc: the per-channel
+// block (1, K) is accepted too).
 int32_t check_gemm_common(const char *fn, const int8_t *xq, const float *xs, const int8_t *w,
                           const float *ws, const uint16_t *y, int64_t rows, int64_t N, int64_t K,
-                          int32_t block_n, int32_t block_k) {
+                          int32_t block_n, int32_t block_k, bool allow_pc = false) {
     if (rows < 0 || rows > kMaxRows)
         return fail(BI8_ERR_SHAPE, "%s: row count %lld out of range", fn, (long long)rows);
     if (N <= 0 || N > kMaxRows)
         return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
     int32_t s = check_k(fn, K);
     if (s) return s;
-    if ((s = check_block(fn, block_n, block_k))) return s;
+    if (allow_pc && per_channel(block_n, block_k, K)) {
+        if (K > kMaxPerChannelK)
+            return fail(BI8_ERR_SHAPE, "%s: per-channel blocks take K <= %lld, got %lld", fn,
+                        (long long)kMaxPerChannelK, (long long)K);
+    } else if ((s = check_block(fn, block_n, block_k))) {
+        return s;
+    }
     if (rows == 0) return BI8_OK;
     if (!xq || !xs || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
     if (!aligned(xq, 16) || !aligned(w, 16))
@@ -107,13 +120,17 @@ int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
     int32_t s = check_k(fn, K);
     if (s) return s;
     if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
-    if ((s = check_block(fn, 128, block_k))) return s;
+    const bool per_token = block_k == K && block_k != 128;   // the per-channel form: one group per row
+    if (!per_token && (s = check_block(fn, 128, block_k))) return s;
     if (M == 0) return ok();
     if (!x || !xq || !xs) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
     if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
     if (!aligned(x, 16) || !aligned(xq, 16))
         return fail(BI8_ERR_ALIGN, "%s: x and xq must be 16-byte aligned", fn);
     if (!aligned(xs, 4)) return fail(BI8_ERR_ALIGN, "%s: xs must be 4-byte aligned", fn);
+    if (per_token)
+        return hip_status(fn, bi8::launch_quant_act_per_token(x, M, K, ldx, xq, xs,
+                                                               static_cast<hipStream_t>(stream)));
     return hip_status(fn, bi8::launch_quant_act(x, M, K, ldx, xq, xs,
                                                  static_cast<hipStream_t>(stream)));
 }
@@ -133,12 +150,18 @@ int32_t blockint8_gemm_variant(int32_t variant, const int8_t *xq, const float *x
     static const char fn[] = "blockint8_gemm";
     if (variant < BI8_GEMM_AUTO || variant > BI8_GEMM_TILE_256X256)
         return fail(BI8_ERR_SHAPE, "%s: unknown kernel variant %d", fn, variant);
-    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, M, N, K, block_n, block_k);
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, M, N, K, block_n, block_k, true);
     if (s) return s;
+    const bool pc = per_channel(block_n, block_k, K);
+    if (pc && variant != BI8_GEMM_AUTO)
+        return fail(BI8_ERR_SHAPE, "%s: the per-channel form has one kernel (variant must be AUTO)", fn);
     if (variant == BI8_GEMM_SKINNY && M > 32)
         return fail(BI8_ERR_SHAPE, "%s: the skinny kernel takes M <= 32, got %lld", fn, (long long)M);
     if (M == 0) return ok();
     if (bias && !aligned(bias, 2)) return fail(BI8_ERR_ALIGN, "%s: bias must be 2-byte aligned", fn);
+    if (pc)
+        return hip_status(fn, bi8::launch_gemm_per_channel(xq, xs, w, ws, bias, y, M, N, K,
+                                                            static_cast<hipStream_t>(stream)));
     return hip_status(fn, bi8::launch_gemm(static_cast<bi8::GemmPath>(variant), xq, xs, w, ws, bias,
                                            y, M, N, K, static_cast<hipStream_t>(stream)));
 }
@@ -160,7 +183,11 @@ int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
     int32_t s = check_k(fn, K);
     if (s) return s;
     if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
-    if ((s = check_block(fn, block_n, block_k))) return s;
+    const bool pc = per_channel(block_n, block_k, K);
+    if (pc && K > kMaxPerChannelK)
+        return fail(BI8_ERR_SHAPE, "%s: per-channel blocks take K <= %lld, got %lld", fn,
+                    (long long)kMaxPerChannelK, (long long)K);
+    if (!pc && (s = check_block(fn, block_n, block_k))) return s;
     if (M == 0) return ok();
     if (!x || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
     if (!xq_workspace || !xs_workspace) return fail(BI8_ERR_NULL, "%s: NULL workspace pointer", fn);
@@ -173,9 +200,16 @@ int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (!aligned(xq_workspace, 16) || !aligned(xs_workspace, 4))
         return fail(BI8_ERR_ALIGN, "%s: xq workspace must be 16-byte and xs workspace 4-byte aligned", fn);
-    hipError_t e = bi8::launch_quant_act(x, M, K, ldx, xq_workspace, xs_workspace, st);
-    if (e == hipSuccess)
-        e = bi8::launch_gemm(bi8::GemmPath::kAuto, xq_workspace, xs_workspace, w, ws, bias, y, M, N, K, st);
+    hipError_t e;
+    if (pc) {
+        e = bi8::launch_quant_act_per_token(x, M, K, ldx, xq_workspace, xs_workspace, st);
+        if (e == hipSuccess)
+            e = bi8::launch_gemm_per_channel(xq_workspace, xs_workspace, w, ws, bias, y, M, N, K, st);
+    } else {
+        e = bi8::launch_quant_act(x, M, K, ldx, xq_workspace, xs_workspace, st);
+        if (e == hipSuccess)
+            e = bi8::launch_gemm(bi8::GemmPath::kAuto, xq_workspace, xs_workspace, w, ws, bias, y, M, N, K, st);
+    }
     return hip_status(fn, e);
 }
 

@@ -732,12 +732,152 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// Per-channel path (the degenerate block: block_n = 1, block_k = K)
+// ---------------------------------------------------------------------------
+//
+// One fp32 scale per weight row (ws [N, 1]) and per token (xs [M, 1]): the
+// per-channel W8A8 of the SGLang platform matrix ("w8a8_int8") is the block
+// form with blocks of 1 x K.  The int32 sums then run over the whole K (no
+// per-block rescale; |sum| <= 127^2 K < 2^31 for K <= 2^17) and the fp32
+// rescale happens once, in the store: y = float(acc) * xs[m] * ws[n].
+// Tiles of 256 weight rows x 128 activation rows, 8 waves of 64 x 64, the
+// same 3-stage buffer->LDS ring and swizzle as the block kernel; one barrier
+// per K block.
+template <bool MOE>
+__global__ __launch_bounds__(512) void gemm_perch_kernel(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = TileCfg<4, 2, 2, 2>;
+    __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds2[C::kStageBytes];
+
+    Tile t;
+    if (!decode_tile<C::kBN, C::kBM, MOE>(p, t)) return;
+    if (t.rows <= 0) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t K = p.K, KB = p.KB;
+    const int64_t wrows = p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
+
+    // pieces q = wave + 8 j share the parity of wave: one chunk per lane
+    const int r_in = lane >> 3;
+    const int chunk = 16 * ((lane & 7) ^ r_in ^ (wave & 1));
+    const uint32_t go = (uint32_t)((8 * wave + r_in) * K + chunk);
+    const uint32_t piece_stride = (uint32_t)(8 * C::kWaves * K);
+    auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
+        const int64_t k0 = kb * kBlock;
+        const bool in_k = k0 + chunk < K;   // also false for every chunk of kb >= KB
+#pragma unroll
+        for (int j = 0; j < C::kWLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024),
+                                                     16, in_k ? go + (uint32_t)k0 + j * piece_stride : kOobOffset,
+                                                     0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::kXLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
+                in_k ? go + (uint32_t)k0 + j * piece_stride : kOobOffset, 0, 0, 0);
+    };
+
+    const int wn = wave % 4, wm = wave / 4;
+    const int rr = lane & 31, hi = lane >> 5;
+    const int swz = (rr & 7) ^ ((rr >> 3) & 1);
+    int frag_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
+    const int wrow0 = (wn * 64 + rr) * 128;
+    const int xrow0 = C::kXOff + (wm * 64 + rr) * 128;
+
+    i32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0;
+    auto mma = [&](const char *stage) __attribute__((always_inline)) {
+        i32x4 wf[2][4], xf[2][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                wf[a][s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+                xf[a][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + a * 32 * 128 + frag_off[s]);
+            }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[a][s], xf[b][s], acc[a][b], 0, 0, 0);
+    };
+    // block kb lives in lds[kb % 3]; loads run two blocks ahead
+    auto step = [&](char *cur, char *ahead, int64_t kb) __attribute__((always_inline)) {
+        wait_vmcnt<C::kTileLoads>();
+        lds_barrier();
+        issue(ahead, kb + 2);
+        mma(cur);
+    };
+    issue(lds0, 0);
+    issue(lds1, 1);
+    int64_t kb = 0;
+    for (; kb + 3 <= KB; kb += 3) {
+        step(lds0, lds2, kb);
+        step(lds1, lds0, kb + 1);
+        step(lds2, lds1, kb + 2);
+    }
+    if (kb < KB) step(lds0, lds2, kb++);
+    if (kb < KB) step(lds1, lds0, kb++);
+    wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
+
+    // Store: lane -> token column rr; element i -> weight row 8 (i / 4) + 4 hi + i % 4.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t ml = wm * 64 + b * 32 + rr;
+        if (ml >= t.rows) continue;
+        const float xsv = p.xs[t.m0 + ml];
+        uint16_t *yrow = p.y + (t.m0 + ml) * p.N;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t n = t.n0 + wn * 64 + a * 32 + 8 * i4 + 4 * hi;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float wsv = n + e < p.N ? t.ws[n + e] : 0.0f;
+                    v[e] = (float)acc[a][b][4 * i4 + e] * (xsv * wsv);
+                    if (p.bias && n + e < p.N) v[e] += bf16_bits_to_f32(p.bias[n + e]);
+                }
+                if (p.wide_store) {
+                    if (n < p.N) {
+                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                }
+            }
+        }
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 // Explicit instantiations: the host pass must emit a launch stub for every
 // variant launched below.
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true>(GemmArgs);
 template __global__ void gemm_wide_kernel<false>(GemmArgs);
+template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true>(GemmArgs);
 
 template <int WN, int WM, int SA, int SB, bool MOE, bool PING>
@@ -837,6 +977,20 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
         default:
             return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                                   const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                   hipStream_t stream) {
+    GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
+    p.NB = N;   // one scale per weight row
+    p.tiles_m = (M + 127) / 128;
+    p.tiles_n = (N + 255) / 256;
+    const int64_t total = p.tiles_m * p.tiles_n;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_perch_kernel<false>), dim3((unsigned)total), dim3(512), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, const int32_t *offsets,

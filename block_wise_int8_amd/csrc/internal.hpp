@@ -21,6 +21,14 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t ldx, const int32_t *rows,
                                    int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream);
 
+// Per-channel form (blocks of 1 x K): xs [M, 1], ws [N, 1], K <= 2^17.
+hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                                   const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                   hipStream_t stream);
+// Per-token activation quantisation (one group of K per row).
+hipError_t launch_quant_act_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *xq,
+                                      float *xs, hipStream_t stream);
+
 // Offline block quantisation of a bf16 weight (128 x 128 blocks).
 hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t ldw, int8_t *wq, float *ws,
                                hipStream_t stream);

@@ -182,3 +182,58 @@ hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t 
 }
 
 }  // namespace bi8
+
+// Per-token quantisation (the per-channel form: one group spanning all K):
+// one workgroup of 256 threads per row, two passes over the row (max, then
+// codes), 16-byte loads.  Same arithmetic as the 128-group kernel.
+namespace bi8 {
+
+namespace {
+
+__global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__restrict__ x, int64_t K,
+                                                              int64_t ldx, int8_t *__restrict__ xq,
+                                                              float *__restrict__ xs) {
+    __shared__ float wmax[4];
+    const int t = threadIdx.x;
+    const int64_t m = blockIdx.x;
+    const uint16_t *row = x + m * ldx;
+    float amax = 0.0f;
+    for (int64_t k = 8 * t; k < K; k += 8 * 256) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)), fabsf(bf16_bits_to_f32(v[j] >> 16))));
+    }
+    amax = wave_max64(amax);
+    if ((t & 63) == 0) wmax[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s = amax / 127.0f;
+    if (t == 0) xs[m] = s;
+    for (int64_t k = 8 * t; k < K; k += 8 * 256) {
+        uint32_t lo = 0u, hi = 0u;
+        if (s != 0.0f) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                lo |= ((uint32_t)quant_one(bf16_bits_to_f32(v[j] & 0xFFFFu), s) & 0xFFu) << (16 * j);
+                lo |= ((uint32_t)quant_one(bf16_bits_to_f32(v[j] >> 16), s) & 0xFFu) << (16 * j + 8);
+                hi |= ((uint32_t)quant_one(bf16_bits_to_f32(v[2 + j] & 0xFFFFu), s) & 0xFFu) << (16 * j);
+                hi |= ((uint32_t)quant_one(bf16_bits_to_f32(v[2 + j] >> 16), s) & 0xFFu) << (16 * j + 8);
+            }
+        }
+        *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *xq,
+                                      float *xs, hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    if (M > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_act_token_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+    return hipGetLastError();
+}
+
+}  // namespace bi8

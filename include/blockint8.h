@@ -76,8 +76,12 @@ const char *blockint8_last_error(void);
  * Bit-exact for finite inputs (divisions are correctly rounded, subnormals
  * are kept).  Non-finite inputs give unspecified codes.
  *
+ * block_k is 128, or K: one group per token, the per-token scales of the
+ * per-channel W8A8 form (the w8a8_int8 scheme of the SGLang quantization
+ * page's platform matrix), xs then [M, 1].
+ *
  * Errors: NULL x/xq/xs (M > 0) -> BI8_ERR_NULL; M < 0, K <= 0, K > BI8_MAX_K,
- * ldx < K -> BI8_ERR_SHAPE; block_k != 128 -> BI8_ERR_BLOCK; K % 16,
+ * ldx < K -> BI8_ERR_SHAPE; block_k not 128 or K -> BI8_ERR_BLOCK; K % 16,
  * ldx % 8, x / xq not 16-byte aligned, xs not 4-byte aligned -> BI8_ERR_ALIGN.
  */
 int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
@@ -101,8 +105,13 @@ int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
  * Block sums are exact int32; the rescaled sum is accumulated in fp32 (the
  * order of the fp32 additions is unspecified).
  *
+ * Blocks are [128, 128], or [1, K]: the per-channel form (one scale per
+ * weight row, ws [N, 1], and per token, xs [M, 1]), the degenerate block of
+ * the same formula; its int32 sums span all of K, so K <= 2^17 there.
+ *
  * Errors: NULL xq/xs/w/ws/y (M > 0) -> BI8_ERR_NULL; M < 0, N <= 0, K <= 0,
- * K > BI8_MAX_K -> BI8_ERR_SHAPE; blocks != [128, 128] -> BI8_ERR_BLOCK;
+ * K > BI8_MAX_K (2^17 per-channel) -> BI8_ERR_SHAPE; blocks other than
+ * [128, 128] and [1, K] -> BI8_ERR_BLOCK;
  * K % 16, xq / w not 16-byte aligned, xs / ws not 4-byte aligned, y / bias
  * not 2-byte aligned -> BI8_ERR_ALIGN.
  */
@@ -284,7 +293,8 @@ int32_t blockint8_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_
  * timed on any shape it accepts.  A variant that cannot run the shape
  * (BI8_GEMM_SKINNY with more than 32 rows, BI8_GEMM_SKINNY or
  * BI8_GEMM_TILE_128X64 for the grouped GEMM) returns BI8_ERR_SHAPE; an
- * unknown variant id returns BI8_ERR_SHAPE.
+ * unknown variant id returns BI8_ERR_SHAPE.  The per-channel form ([1, K]
+ * blocks) has a single kernel: only BI8_GEMM_AUTO runs it.
  *
  *   BI8_GEMM_AUTO          the shape-based choice
  *   BI8_GEMM_SKINNY        M <= 32: weight rows streamed into registers

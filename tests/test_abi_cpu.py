@@ -93,7 +93,8 @@ def test_quant_empty_is_noop(lib):
     (dict(M=-1), SHAPE), (dict(N=0), SHAPE), (dict(N=-5), SHAPE), (dict(K=0), SHAPE),
     (dict(M=1 << 31), SHAPE), (dict(K=1 << 24), SHAPE),
     (dict(bn=0), BLOCK), (dict(bk=-1), BLOCK), (dict(bn=64), BLOCK), (dict(bk=256), BLOCK),
-    (dict(bn=1, bk=256), BLOCK),
+    (dict(bn=1, bk=128), BLOCK), (dict(bn=1, bk=512), BLOCK),   # (1, K) only with block_k == K
+    (dict(bn=1, bk=1 << 18, K=1 << 18), SHAPE),                    # per-channel int32 sums: K <= 2^17
     (dict(K=4008), ALIGN), (dict(xq=P16 + 4), ALIGN), (dict(w=P16 + 8), ALIGN),
     (dict(xs=P16 + 1), ALIGN), (dict(ws=P16 + 3), ALIGN), (dict(y=P_ODD), ALIGN),
     (dict(bias=P_ODD), ALIGN),
@@ -333,3 +334,13 @@ def test_quant_weight_rejects(lib, kw, status):
 
 def test_quant_weight_empty_is_noop(lib):
     assert qweight(lib, N=0, w=None, wq=None, ws=None) == OK
+
+
+def test_per_channel_blocks_are_checked_before_launch(lib):
+    # the (1, K) form: variant must be AUTO, MoE does not take it
+    assert gemm_v(lib, bi8.GEMM_TILE_256X128, M=64, bn=1, bk=256) == SHAPE
+    assert gemm_v(lib, bi8.GEMM_AUTO, M=0, bn=1, bk=256, xq=None, xs=None, w=None, ws=None, y=None) == OK
+    assert moe(lib, bn=1, bk=256) == BLOCK
+    assert quant(lib, M=0, bk=256, x=None, xq=None, xs=None) == OK          # block_k == K: per token
+    assert quant(lib, bk=64) == BLOCK
+    assert linear(lib, bn=1, bk=1 << 18, K=1 << 18, ldx=1 << 18) == SHAPE
