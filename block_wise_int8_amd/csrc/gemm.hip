@@ -75,7 +75,10 @@ __device__ __forceinline__ i32x4 as_i32x4(u32x4 v) {
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyUnroll = 4;
 
-template <int MT>   // 16-token column tiles: 1 for M <= 16, 2 for M <= 32
+// MT: 16-token column tiles (1 for M <= 16, 2 for M <= 32).  PC: the
+// per-channel form (blocks of 1 x K): the block sums are added unscaled and
+// the token and weight-row scales multiply once, in the store.
+template <int MT, bool PC>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs p,
                                                                        int32_t blocks_per_wave) {
     __shared__ float red[kSkinnyWaves][MT][64][4];
@@ -120,9 +123,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
                 xb[u][mt][0] = as_i32x4(buf_load16(xr, in0 ? (uint32_t)(tok * K + kk) : kOobOffset));
                 xb[u][mt][1] =
                     as_i32x4(buf_load16(xr, in1 ? (uint32_t)(tok * K + kk + 16) : kOobOffset));
-                xsv[u][mt] = buf_load_f32(sr, ok ? (uint32_t)((tok * KB + b) * 4) : kOobOffset);
+                if constexpr (!PC) xsv[u][mt] = buf_load_f32(sr, ok ? (uint32_t)((tok * KB + b) * 4) : kOobOffset);
             }
-            wsv[u] = ws_row[ok ? b : KB - 1];
+            if constexpr (!PC) wsv[u] = ws_row[ok ? b : KB - 1];
         }
         // every load above is issued before the first MFMA: without this the
         // scheduler interleaves loads and MFMAs and the wave pays several HBM
@@ -135,9 +138,14 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
                 i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], xb[u][mt][0],
                                                                   i32x4{0, 0, 0, 0}, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], xb[u][mt][1], acc, 0, 0, 0);
-                const float t = xsv[u][mt] * wsv[u];
+                if constexpr (PC) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) yv[mt][i] = fmaf((float)acc[i], t, yv[mt][i]);
+                    for (int i = 0; i < 4; ++i) yv[mt][i] += (float)acc[i];
+                } else {
+                    const float t = xsv[u][mt] * wsv[u];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yv[mt][i] = fmaf((float)acc[i], t, yv[mt][i]);
+                }
             }
         }
     }
@@ -157,6 +165,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
         for (int v = 0; v < kSkinnyWaves; ++v) s += red[v][mt][src][i];
         const int64_t tok = mt * 16 + c, n = n0 + r;
         if (tok < p.M && n < p.N) {
+            if constexpr (PC) s *= p.xs[tok] * p.ws[n];
             if (p.bias) s += bf16_bits_to_f32(p.bias[n]);
             p.y[tok * p.N + n] = (uint16_t)f32_to_bf16_bits(s);
         }
@@ -955,10 +964,10 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
             if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
             const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
             if (M <= 16)
-                hipLaunchKernelGGL(gemm_skinny_kernel<1>, dim3((unsigned)tiles),
+                hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), dim3((unsigned)tiles),
                                    dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
             else
-                hipLaunchKernelGGL(gemm_skinny_kernel<2>, dim3((unsigned)tiles),
+                hipLaunchKernelGGL((gemm_skinny_kernel<2, false>), dim3((unsigned)tiles),
                                    dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
             return hipGetLastError();
         }
@@ -984,6 +993,18 @@ hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8
                                    hipStream_t stream) {
     GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
     p.NB = N;   // one scale per weight row
+    if (M <= 32) {
+        const int64_t tiles = (N + 15) / 16;
+        if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
+        const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
+        if (M <= 16)
+            hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), dim3((unsigned)tiles), dim3(kSkinnyWaves * 64), 0,
+                               stream, p, bpw);
+        else
+            hipLaunchKernelGGL((gemm_skinny_kernel<2, true>), dim3((unsigned)tiles), dim3(kSkinnyWaves * 64), 0,
+                               stream, p, bpw);
+        return hipGetLastError();
+    }
     p.tiles_m = (M + 127) / 128;
     p.tiles_n = (N + 255) / 256;
     const int64_t total = p.tiles_m * p.tiles_n;
