@@ -149,9 +149,12 @@ __device__ __forceinline__ float silu_times(float g, float u) {
     return ((g * t) * u) * 0x1p-64f;
 }
 
-// One wave covers four 128-groups of one row; 16 lanes per group, 8 entries
-// per lane.  h row r: gate h[r, i], up h[r, I + i].
+// One wave covers eight 128-groups of one row in two halves of four; 16 lanes
+// per group, 8 entries per lane and half, all four 16-byte loads (gate and up
+// of both halves) in flight before any is used.  h row r: gate h[r, i], up
+// h[r, I + i].
 constexpr int kSiluWaves = 4;
+constexpr int kSiluChunks = 2;
 __global__ __launch_bounds__(kSiluWaves * 64) void silu_mul_quant_kernel(
     const uint16_t *__restrict__ h, int64_t I, int8_t *__restrict__ aq, float *__restrict__ as,
     uint16_t *__restrict__ a_out, int64_t IB, int64_t waves_per_row, int64_t total_waves) {
@@ -159,44 +162,53 @@ __global__ __launch_bounds__(kSiluWaves * 64) void silu_mul_quant_kernel(
     const int64_t wave = (int64_t)blockIdx.x * kSiluWaves + (threadIdx.x >> 6);
     if (wave >= total_waves) return;
     const int64_t r = wave / waves_per_row;
-    const int64_t g = (wave - r * waves_per_row) * 4 + (lane >> 4);
-    const int64_t i = g * kBlock + (lane & 15) * 8;
-    const bool valid = g < IB && i < I;   // I % 16 == 0: a lane's 8 entries are all in or all out
-    u32x4 gv = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
-    if (valid) {
-        gv = *reinterpret_cast<const u32x4 *>(h + r * 2 * I + i);
-        uv = *reinterpret_cast<const u32x4 *>(h + r * 2 * I + I + i);
-    }
-    float a[8];
-    uint32_t ab[8];
+    const int64_t g0 = (wave - r * waves_per_row) * 4 * kSiluChunks + (lane >> 4);
+    u32x4 gv[kSiluChunks], uv[kSiluChunks];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t gb = (j & 1) ? (gv[j >> 1] >> 16) : (gv[j >> 1] & 0xFFFFu);
-        const uint32_t ub = (j & 1) ? (uv[j >> 1] >> 16) : (uv[j >> 1] & 0xFFFFu);
-        ab[j] = f32_to_bf16_bits(silu_times(bf16_bits_to_f32(gb), bf16_bits_to_f32(ub)));
-        a[j] = bf16_bits_to_f32(ab[j]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(a[j]));
-    amax = group_max16(amax);
-    const float s = amax / 127.0f;
-    if (!valid) return;
-    uint32_t lo = 0u, hi = 0u;
-    if (s != 0.0f) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            lo |= quant_code(a[j], s) << (8 * j);
-            hi |= quant_code(a[4 + j], s) << (8 * j);
+    for (int c = 0; c < kSiluChunks; ++c) {
+        const int64_t g = g0 + 4 * c, i = g * kBlock + (lane & 15) * 8;
+        gv[c] = u32x4{0u, 0u, 0u, 0u};
+        uv[c] = u32x4{0u, 0u, 0u, 0u};
+        if (g < IB && i < I) {   // I % 16 == 0: a lane's 8 entries are all in or all out
+            gv[c] = *reinterpret_cast<const u32x4 *>(h + r * 2 * I + i);
+            uv[c] = *reinterpret_cast<const u32x4 *>(h + r * 2 * I + I + i);
         }
     }
-    *reinterpret_cast<uint2 *>(aq + r * I + i) = make_uint2(lo, hi);
-    if ((lane & 15) == 0) as[r * IB + g] = s;
-    if (a_out) {
-        u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = ab[2 * j] | (ab[2 * j + 1] << 16);
-        *reinterpret_cast<u32x4 *>(a_out + r * I + i) = o;
+    for (int c = 0; c < kSiluChunks; ++c) {
+        const int64_t g = g0 + 4 * c, i = g * kBlock + (lane & 15) * 8;
+        const bool valid = g < IB && i < I;
+        float a[8];
+        uint32_t ab[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t gb = (j & 1) ? (gv[c][j >> 1] >> 16) : (gv[c][j >> 1] & 0xFFFFu);
+            const uint32_t ub = (j & 1) ? (uv[c][j >> 1] >> 16) : (uv[c][j >> 1] & 0xFFFFu);
+            ab[j] = f32_to_bf16_bits(silu_times(bf16_bits_to_f32(gb), bf16_bits_to_f32(ub)));
+            a[j] = bf16_bits_to_f32(ab[j]);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(a[j]));
+        amax = group_max16(amax);
+        const float s = amax / 127.0f;
+        if (!valid) continue;
+        uint32_t lo = 0u, hi = 0u;
+        if (s != 0.0f) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= quant_code(a[j], s) << (8 * j);
+                hi |= quant_code(a[4 + j], s) << (8 * j);
+            }
+        }
+        *reinterpret_cast<uint2 *>(aq + r * I + i) = make_uint2(lo, hi);
+        if ((lane & 15) == 0) as[r * IB + g] = s;
+        if (a_out) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = ab[2 * j] | (ab[2 * j + 1] << 16);
+            *reinterpret_cast<u32x4 *>(a_out + r * I + i) = o;
+        }
     }
 }
 
@@ -249,7 +261,7 @@ hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t k
 hipError_t launch_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int8_t *aq, float *as,
                                  uint16_t *a_out, hipStream_t stream) {
     const int64_t IB = (I + kBlock - 1) / kBlock;
-    const int64_t waves_per_row = (IB + 3) / 4;
+    const int64_t waves_per_row = (IB + 4 * kSiluChunks - 1) / (4 * kSiluChunks);
     const int64_t total_waves = R * waves_per_row;
     const int64_t blocks = (total_waves + kSiluWaves - 1) / kSiluWaves;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;

@@ -7,10 +7,10 @@
 // clamp(rne(x / s), -127, 127), zero codes for an all-zero group.
 //
 // HBM-bound single pass: 2 B read + 1 B written per element, 4 B per group.
-// Layout on the chip: one wave64 covers 4 consecutive groups of one row; 16
-// lanes per group, 8 bf16 (one 16-byte load) per lane, so a wave reads 1 KB
-// contiguous and writes 512 B contiguous.  The group max is reduced across
-// the 16 lanes with cross-lane moves.  Division is IEEE correctly rounded and
+// Layout on the chip: one wave64 covers 4 consecutive groups of one row (16
+// lanes per group, 8 bf16 = one 16-byte load per lane), or, for large
+// problems, 8 groups in two halves with both loads in flight before either is
+// used.  The group max is reduced across the 16 lanes with cross-lane moves.  Division is IEEE correctly rounded and
 // denormals are kept (build flags), so codes and scales are bit-exact.
 #include "common.hpp"
 #include "internal.hpp"
@@ -20,7 +20,6 @@ namespace bi8 {
 namespace {
 
 constexpr int kQuantWaves = 4;          // waves per workgroup
-constexpr int kGroupsPerWave = 4;
 
 __device__ __forceinline__ float group_max16(float v) {
     // xor-butterfly over the 16 lanes of a group (lanes differ in bits 0..3)
@@ -39,6 +38,9 @@ __device__ __forceinline__ int32_t quant_one(float x, float s) {
 
 // rows (gather form, may be null): output row m quantises source row
 // rows[m] of x (src_rows rows); an index outside [0, src_rows) reads zeros.
+// kChunks: 16-byte loads in flight per lane (1 for small problems, where the
+// second chunk's arithmetic would only lengthen the critical path).
+template <int kChunks>
 __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     const uint16_t *__restrict__ x, int64_t K, int64_t ldx, int8_t *__restrict__ xq,
     float *__restrict__ xs, int64_t KB, int64_t waves_per_row, int64_t total_waves,
@@ -47,39 +49,47 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     const int64_t wave = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
     if (wave >= total_waves) return;
     const int64_t m = wave / waves_per_row;
-    const int64_t g = (wave - m * waves_per_row) * kGroupsPerWave + (lane >> 4);
-    const int64_t k = g * kBlock + (lane & 15) * 8;
+    const int64_t g0 = (wave - m * waves_per_row) * 4 * kChunks + (lane >> 4);
     const int64_t src = rows ? (int64_t)rows[m] : m;
-    // K % 16 == 0, so a lane's 8 elements are either all inside the row or all
-    // outside; outside lanes contribute zeros, which change no group max.
-    const bool valid = (g < KB) && (k < K);
-
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (valid && src >= 0 && src < src_rows) v = *reinterpret_cast<const u32x4 *>(x + src * ldx + k);
-
-    float f[8];
+    const bool src_ok = src >= 0 && src < src_rows;
+    // Lane chunk j covers group g0 + 4 j.  K % 16 == 0, so a lane's 8
+    // elements are either all inside the row or all outside; outside lanes
+    // contribute zeros, which change no group max.  Both loads are issued
+    // before either is used.
+    u32x4 v[kChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
-        f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+    for (int j = 0; j < kChunks; ++j) {
+        const int64_t g = g0 + 4 * j, k = g * kBlock + (lane & 15) * 8;
+        v[j] = u32x4{0u, 0u, 0u, 0u};
+        if (g < KB && k < K && src_ok) v[j] = *reinterpret_cast<const u32x4 *>(x + src * ldx + k);
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = group_max16(amax);
-    const float s = amax / 127.0f;
-
-    if (!valid) return;
-    uint32_t lo = 0u, hi = 0u;
-    if (s != 0.0f) {
+    for (int j = 0; j < kChunks; ++j) {
+        const int64_t g = g0 + 4 * j, k = g * kBlock + (lane & 15) * 8;
+        const bool valid = (g < KB) && (k < K);
+        float f[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            lo |= ((uint32_t)quant_one(f[i], s) & 0xFFu) << (8 * i);
-            hi |= ((uint32_t)quant_one(f[4 + i], s) & 0xFFu) << (8 * i);
+            f[2 * i] = bf16_bits_to_f32(v[j][i] & 0xFFFFu);
+            f[2 * i + 1] = bf16_bits_to_f32(v[j][i] >> 16);
         }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = group_max16(amax);
+        const float s = amax / 127.0f;
+        if (!valid) continue;
+        uint32_t lo = 0u, hi = 0u;
+        if (s != 0.0f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= ((uint32_t)quant_one(f[i], s) & 0xFFu) << (8 * i);
+                hi |= ((uint32_t)quant_one(f[4 + i], s) & 0xFFu) << (8 * i);
+            }
+        }
+        *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
+        if ((lane & 15) == 0) xs[m * KB + g] = s;
     }
-    *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
-    if ((lane & 15) == 0) xs[m * KB + g] = s;
 }
 
 }  // namespace
@@ -92,13 +102,19 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t ldx, const int32_t *rows,
                                    int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream) {
     const int64_t KB = (K + kBlock - 1) / kBlock;
-    const int64_t waves_per_row = (KB + kGroupsPerWave - 1) / kGroupsPerWave;
+    const bool two = M * KB >= 8192;   // enough groups to fill the chip with two per lane
+    const int64_t gpw = two ? 8 : 4;   // groups per wave
+    const int64_t waves_per_row = (KB + gpw - 1) / gpw;
     const int64_t total_waves = M * waves_per_row;
     const int64_t blocks = (total_waves + kQuantWaves - 1) / kQuantWaves;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)blocks), dim3(kQuantWaves * 64), 0, stream,
-                       x, K, ldx, xq, xs, KB, waves_per_row, total_waves, rows, src_rows);
+    if (two)
+        hipLaunchKernelGGL((quant_act_kernel<2>), dim3((unsigned)blocks), dim3(kQuantWaves * 64), 0, stream,
+                           x, K, ldx, xq, xs, KB, waves_per_row, total_waves, rows, src_rows);
+    else
+        hipLaunchKernelGGL((quant_act_kernel<1>), dim3((unsigned)blocks), dim3(kQuantWaves * 64), 0, stream,
+                           x, K, ldx, xq, xs, KB, waves_per_row, total_waves, rows, src_rows);
     return hipGetLastError();
 }
 
