@@ -155,7 +155,7 @@ def test_variant_ids_match_header():
 @pytest.mark.parametrize("M,N,K,variant", [
     (1, 4096, 4096, bi8.GEMM_SKINNY), (32, 100, 128, bi8.GEMM_SKINNY),
     (33, 4096, 4096, bi8.GEMM_TILE_128X64), (333, 5000, 4000, bi8.GEMM_TILE_128X64),
-    (2048, 4096, 14336, bi8.GEMM_TILE_256X128), (4096, 4096, 4096, bi8.GEMM_TILE_256X128),
+    (2048, 4096, 14336, bi8.GEMM_TILE_256X128), (4096, 4096, 4096, bi8.GEMM_TILE_256X256),
     (2048, 28672, 4096, bi8.GEMM_TILE_256X256), (8192, 8192, 1024, bi8.GEMM_TILE_256X256),
 ])
 def test_gemm_select(lib, M, N, K, variant):
