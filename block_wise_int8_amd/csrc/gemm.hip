@@ -642,6 +642,10 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     if (nbw > p.NB - 1) nbw = p.NB - 1;
     const BI8_CONST float *ws_row = reinterpret_cast<const BI8_CONST float *>(
         reinterpret_cast<uintptr_t>(t.ws + nbw * KB));
+    // The weight scale of a block is a scalar load issued one block ahead:
+    // scalar loads complete out of order, so a use right after the load would
+    // wait for every outstanding LDS read as well.
+    float ws_cur = ws_row[0];
 
     i32x16 zero16;
 #pragma unroll
@@ -668,18 +672,27 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
-        float tb[SB];
-        const float wsv = ws_row[kb];
+        // first W fragments, then the scales, all issued before the first wait
+        i32x4 wf0[4];
 #pragma unroll
-        for (int b = 0; b < SB; ++b)
-            tb[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))] * wsv;
+        for (int s = 0; s < 4; ++s) wf0[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + frag_off[s]);
+        float xsv[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
+        const float wsv = ws_cur;
+        ws_cur = ws_row[kb + 1 < KB ? kb + 1 : kb];   // next block's, issued a block ahead
+        __builtin_amdgcn_sched_barrier(0);
+        float tb[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) tb[b] = xsv[b] * wsv;
         i32x16 acc[2];
 #pragma unroll
         for (int a = 0; a < SA; ++a) {
             i32x4 wf[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                wf[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+                wf[s] = a == 0 ? wf0[s]
+                               : *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
 #pragma unroll
             for (int b = 0; b < SB; ++b) {
                 const int j = a * SB + b;
