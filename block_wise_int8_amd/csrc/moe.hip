@@ -107,19 +107,21 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(const int32_t 
             const uint64_t m = __ballot(slot >= 0);
             if (lane == 0) wave_tot[wave] = __popcll(m);
             __syncthreads();
+            // every thread reads the wave counts now, before the barrier below:
+            // after it the next round overwrites them
+            int32_t pre = 0, tot = 0;
+            for (int w = 0; w < kAlignThreads / 64; ++w) {
+                const int32_t c = wave_tot[w];
+                pre += w < wave ? c : 0;
+                tot += c;
+            }
             if (slot >= 0) {
-                int32_t pre = 0;
-                for (int w = 0; w < wave; ++w) pre += wave_tot[w];
                 const int32_t pos = base[e] + pre + __popcll(m & below);
                 sorted_token[pos] = (int32_t)t;
                 row_of[t * k + slot] = pos;
             }
             __syncthreads();
-            if (tid == 0) {
-                int32_t tot = 0;
-                for (int w = 0; w < kAlignThreads / 64; ++w) tot += wave_tot[w];
-                base[e] += tot;
-            }
+            if (tid == 0) base[e] += tot;
         }
     }
 }

@@ -32,7 +32,7 @@ def route_both(logits, k, renorm=False):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (7, 3, 1), (1000, 8, 2), (4096, 8, 2), (2500, 64, 4),
-                                   (333, 16, 8), (5, 1, 1), (1025, 128, 2)])
+                                   (333, 16, 8), (5, 1, 1), (1025, 128, 2), (3000, 65, 2), (4096, 512, 8)])
 @pytest.mark.parametrize("renorm", [False, True])
 def test_route_matches_oracle(T, E, k, renorm):
     logits = wl.router_logits(np.random.default_rng(T * 31 + E), T, E)
