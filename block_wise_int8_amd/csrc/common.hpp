@@ -35,6 +35,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
+// One int8 code clamp(rne(x / s), -127, 127) with x / s the IEEE correctly
+// rounded quotient, computed from r = 1 / s (correctly rounded) by a single
+// multiply.  y = x * r is within |x / s| * 1.5 * 2^-23 <= 2.3e-5 of fl(x / s)
+// for |x / s| <= 127.5, so the two round to the same integer unless y lies
+// within 2^-14 of a half-integer; those products (and non-finite ones, e.g.
+// r = inf for a subnormal s) take the division.
+__device__ __forceinline__ int32_t quant_code(float x, float s, float r) {
+    const float y = x * r;
+    float q = rintf(y);
+    if (!(fabsf(y - q) < 0.5f - 0x1p-14f)) q = rintf(x / s);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int32_t)q;
+}
+
 // Raw buffer resource over [base, base + num_bytes): loads at offsets past the
 // end return zero (gfx9 raw-buffer range check, stride 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {

@@ -134,12 +134,6 @@ __device__ __forceinline__ float group_max16(float v) {
     return v;
 }
 
-__device__ __forceinline__ uint32_t quant_code(float x, float s) {
-    float q = rintf(x / s);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (uint32_t)(int32_t)q & 0xFFu;
-}
-
 // silu(g) * u = g / (1 + exp(-g)) * u in fp32.  Below g = -80, exp(g) nears
 // the fp32 subnormal range (and exp(-g) overflows past g = -88.7, which would
 // give zero where the result is still a normal bf16), so there the product is
@@ -197,10 +191,11 @@ __global__ __launch_bounds__(kSiluWaves * 64) void silu_mul_quant_kernel(
         if (!valid) continue;
         uint32_t lo = 0u, hi = 0u;
         if (s != 0.0f) {
+            const float rs = 1.0f / s;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                lo |= quant_code(a[j], s) << (8 * j);
-                hi |= quant_code(a[4 + j], s) << (8 * j);
+                lo |= ((uint32_t)quant_code(a[j], s, rs) & 0xFFu) << (8 * j);
+                hi |= ((uint32_t)quant_code(a[4 + j], s, rs) & 0xFFu) << (8 * j);
             }
         }
         *reinterpret_cast<uint2 *>(aq + r * I + i) = make_uint2(lo, hi);

@@ -10,8 +10,10 @@
 // Layout on the chip: one wave64 covers 4 consecutive groups of one row (16
 // lanes per group, 8 bf16 = one 16-byte load per lane), or, for large
 // problems, 8 groups in two halves with both loads in flight before either is
-// used.  The group max is reduced across the 16 lanes with cross-lane moves.  Division is IEEE correctly rounded and
-// denormals are kept (build flags), so codes and scales are bit-exact.
+// used.  The group max is reduced across the 16 lanes with cross-lane moves.  The
+// scale is an IEEE correctly rounded division and denormals are kept (build
+// flags); codes come from one multiply by 1 / s with the division taken where
+// the two could round apart (quant_code), so codes and scales are bit-exact.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -81,10 +83,11 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
         if (!valid) continue;
         uint32_t lo = 0u, hi = 0u;
         if (s != 0.0f) {
+            const float r = 1.0f / s;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                lo |= ((uint32_t)quant_one(f[i], s) & 0xFFu) << (8 * i);
-                hi |= ((uint32_t)quant_one(f[4 + i], s) & 0xFFu) << (8 * i);
+                lo |= ((uint32_t)quant_code(f[i], s, r) & 0xFFu) << (8 * i);
+                hi |= ((uint32_t)quant_code(f[4 + i], s, r) & 0xFFu) << (8 * i);
             }
         }
         *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);

@@ -74,6 +74,26 @@ def test_quant_special_values_bit_exact():
     assert 0 < s[4, 0] < np.finfo(np.float32).tiny
 
 
+@pytest.mark.parametrize("amax_bits", [0x3F80, 0x4040, 0x42C8, 0x42FE, 0x3E9A, 0x0380, 0x0001, 0x7F7F])
+def test_quant_every_bf16_below_amax_bit_exact(amax_bits):
+    """Every bf16 value of magnitude <= amax, 127 per group with amax itself first:
+    covers each quotient x / s the group can produce, ties and near-ties included
+    (amax 1, 3, 100, 127, 0.3, 2^-120, the smallest subnormal, the largest finite)."""
+    b = np.arange(0, 0x7F80, dtype=np.uint32)          # every finite non-negative bf16
+    vals = b[b <= amax_bits]
+    vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
+    n = -(-len(vals) // 127)
+    x = np.zeros((n, 128), np.uint16)
+    x[:, 0] = amax_bits
+    flat = x[:, 1:].reshape(-1)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(n, 127)
+    q_ref, s_ref = oracle.quant_act(x)
+    q, s = gpu_quant(x)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q, q_ref)
+
+
 @pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (5, 144), (7, 4000), (64, 128), (2, 14336),
                                  (65537, 128)])
 def test_quant_shapes_bit_exact(M, K):
