@@ -134,13 +134,16 @@ __device__ __forceinline__ float group_max16(float v) {
     return v;
 }
 
-// silu(g) * u = g / (1 + exp(-g)) * u in fp32.  Below g = -80, exp(g) nears
-// the fp32 subnormal range (and exp(-g) overflows past g = -88.7, which would
-// give zero where the result is still a normal bf16), so there the product is
-// formed as g * (2^64 exp(g)) * u * 2^-64 with 2^64 exp(g) = exp2(g log2(e)
-// + 64); 1 + exp(g) rounds to 1.
+// silu(g) * u = g / (1 + exp(-g)) * u in fp32, the quotient through the
+// hardware reciprocal (within 1 ulp; the bf16 result then differs from the
+// correctly rounded quotient's only where the fp32 value sits at a bf16
+// rounding boundary).  Below g = -80, exp(g) nears the fp32 subnormal range
+// (and exp(-g) overflows past g = -88.7, which would give zero where the
+// result is still a normal bf16), so there the product is formed as
+// g * (2^64 exp(g)) * u * 2^-64 with 2^64 exp(g) = exp2(g log2(e) + 64);
+// 1 + exp(g) rounds to 1.
 __device__ __forceinline__ float silu_times(float g, float u) {
-    if (g >= -80.0f) return g / (1.0f + expf(-g)) * u;
+    if (g >= -80.0f) return g * __builtin_amdgcn_rcpf(1.0f + expf(-g)) * u;
     const float t = exp2f(fmaf(g, 1.44269504088896341f, 64.0f));
     return ((g * t) * u) * 0x1p-64f;
 }
