@@ -32,12 +32,6 @@ __device__ __forceinline__ float group_max16(float v) {
     return v;
 }
 
-__device__ __forceinline__ int32_t quant_one(float x, float s) {
-    float q = rintf(x / s);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int32_t)q;
-}
-
 // rows (gather form, may be null): output row m quantises source row
 // rows[m] of x (src_rows rows); an index outside [0, src_rows) reads zeros.
 // kChunks: 16-byte loads in flight per lane (1 for small problems, where the
@@ -171,6 +165,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t *__res
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = amax / 127.0f;
+    const float r = 1.0f / s;
     if (t == 0) ws[bn * KB + bk] = s;
     if (!row_ok) return;
 #pragma unroll
@@ -180,8 +175,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t *__res
         if (s != 0.0f) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                lo |= ((uint32_t)quant_one(f[8 * c + j], s) & 0xFFu) << (8 * j);
-                hi |= ((uint32_t)quant_one(f[8 * c + 4 + j], s) & 0xFFu) << (8 * j);
+                lo |= ((uint32_t)quant_code(f[8 * c + j], s, r) & 0xFFu) << (8 * j);
+                hi |= ((uint32_t)quant_code(f[8 * c + 4 + j], s, r) & 0xFFu) << (8 * j);
             }
         }
         *reinterpret_cast<uint2 *>(wq + n * K + k0 + 8 * c) = make_uint2(lo, hi);
@@ -228,6 +223,7 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = amax / 127.0f;
+    const float r = 1.0f / s;
     if (t == 0) xs[m] = s;
     for (int64_t k = 8 * t; k < K; k += 8 * 256) {
         uint32_t lo = 0u, hi = 0u;
@@ -235,10 +231,10 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
             const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                lo |= ((uint32_t)quant_one(bf16_bits_to_f32(v[j] & 0xFFFFu), s) & 0xFFu) << (16 * j);
-                lo |= ((uint32_t)quant_one(bf16_bits_to_f32(v[j] >> 16), s) & 0xFFu) << (16 * j + 8);
-                hi |= ((uint32_t)quant_one(bf16_bits_to_f32(v[2 + j] & 0xFFFFu), s) & 0xFFu) << (16 * j);
-                hi |= ((uint32_t)quant_one(bf16_bits_to_f32(v[2 + j] >> 16), s) & 0xFFu) << (16 * j + 8);
+                lo |= ((uint32_t)quant_code(bf16_bits_to_f32(v[j] & 0xFFFFu), s, r) & 0xFFu) << (16 * j);
+                lo |= ((uint32_t)quant_code(bf16_bits_to_f32(v[j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
+                hi |= ((uint32_t)quant_code(bf16_bits_to_f32(v[2 + j] & 0xFFFFu), s, r) & 0xFFu) << (16 * j);
+                hi |= ((uint32_t)quant_code(bf16_bits_to_f32(v[2 + j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
             }
         }
         *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
