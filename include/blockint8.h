@@ -73,8 +73,10 @@ const char *blockint8_last_error(void);
  *   amax = max |x|,  s = amax / 127 (binary32, round to nearest),
  *   xq = 0 if s == 0 else clamp(round_half_even(x / s), -127, 127),
  *   xs[m, g] = s.
- * Bit-exact for finite inputs (divisions are correctly rounded, subnormals
- * are kept).  Non-finite inputs give unspecified codes.
+ * Bit-exact for finite inputs: s is a correctly rounded division, and each
+ * code equals round_half_even of the correctly rounded quotient x / s (it is
+ * formed as x * (1/s), with the division itself wherever the two could round
+ * apart); subnormals are kept.  Non-finite inputs give unspecified codes.
  *
  * block_k is 128, or K: one group per token, the per-token scales of the
  * per-channel W8A8 form (the w8a8_int8 scheme of the SGLang quantization
@@ -258,8 +260,11 @@ int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, co
  * Gate/up activation fused with the quantisation of its result, for the w2
  * GEMM.  h (the w13 output) holds gate in columns [0, I) and up in [I, 2I):
  *
- *   a[r, i] = bf16( silu(gate) * up ),  silu(z) = z / (1 + exp(-z))  (fp32)
- *   aq, as  = blockint8_quant_act(a)   (bit for bit)
+ *   a[r, i] = bf16( silu(gate) * up ),  silu(z) = z / (1 + exp(-z))  (fp32;
+ *             the quotient through the hardware reciprocal, so a may differ
+ *             from a correctly rounded evaluation by one bf16 ulp in rare
+ *             cases)
+ *   aq, as  = blockint8_quant_act(a)   (bit for bit, on this a)
  *
  *   h   bf16 [R, 2I] (16-byte aligned)   aq int8 [R, I]   as fp32 [R, ceil(I/128)]
  *   a   bf16 [R, I]  optional copy of the activation (NULL: not written)
