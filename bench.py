@@ -136,7 +136,7 @@ class Dense:
         oracle.gemm(xq, xs, self.w_np, self.ws_np, block=self.block)
         t_row = max(time.perf_counter() - t0, 1e-4)
         rows = int(max(1, min(self.M, budget_s / t_row)))
-        reps = int(max(1, min(50, budget_s / (t_row * rows))))
+        reps = int(max(1, min(1000, budget_s / (t_row * rows))))
         t0 = time.perf_counter()
         for _ in range(reps):
             xq, xs = oracle.quant_act(self.x_np[:rows], block_k=self.block[1])
