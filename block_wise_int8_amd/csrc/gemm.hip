@@ -540,7 +540,10 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 // pipelined per sub-tile instead: while the MFMAs of sub-tile j run, the VALU
 // converts and rescales sub-tile j - 1 (two 16-register int32 buffers).  Two
 // 64 KB stages form the LDS ring: block kb + 1 is loaded while block kb is
-// computed.
+// computed, and the barrier and first fragment reads of block kb + 1 overlap
+// the last rescale of block kb.  The activation scales reach LDS by
+// buffer-to-LDS loads, eight K blocks at a time, without passing through
+// registers.
 struct WideCfg {
     static constexpr int kWaves = 8;
     static constexpr int kThreads = kWaves * 64;
@@ -589,25 +592,28 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     const int chunk = 16 * ((lane & 7) ^ r_in ^ (wave & 1));
     const uint32_t go = (uint32_t)((8 * wave + r_in) * K + chunk);
     const uint32_t piece_stride = (uint32_t)(8 * C::kWaves * K);
-    float sv[C::kScaleLoads];
     uint32_t sofs[C::kScaleLoads];   // byte offset of this lane's scale entry at kb = 0
 #pragma unroll
     for (int j = 0; j < C::kScaleLoads; ++j) {
         const int f = (wave * C::kScaleLoads + j) * 64 + lane;
         sofs[j] = (uint32_t)(((f / C::kSB) * KB + (f & (C::kSB - 1))) * 4);
     }
+    // K blocks this lane's 16-byte chunk lies in: kb < kb_in <=> kb * 128 + chunk < K
+    const int kb_in = (int)((K - chunk + kBlock - 1) / kBlock);
 
     auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
-        const int64_t k0 = kb * kBlock;
-        const uint32_t kofs = (uint32_t)k0;
+        const uint32_t kofs = (uint32_t)kb * kBlock;
         if ((kb & (C::kSB - 1)) == 0) {
-            // Entries past the last K block read the next row's scales (or
-            // zero past the end of xs): they are never used, so no check.
+            // The batch of activation scales goes straight to LDS, 4 bytes a
+            // lane.  Entries past the last K block read the next row's scales
+            // (or zero past the end of xs): they are never used, so no check.
 #pragma unroll
             for (int j = 0; j < C::kScaleLoads; ++j)
-                sv[j] = buf_load_f32(sr, sofs[j] + (uint32_t)kb * 4u);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    sr, (BI8_LDS void *)&xsl[(kb / C::kSB) & 1][(wave * C::kScaleLoads + j) * 64], 4,
+                    sofs[j] + (uint32_t)kb * 4u, 0, 0, 0);
         }
-        const bool in_k = k0 + chunk < K;
+        const bool in_k = (int)kb < kb_in;
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -618,12 +624,6 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
                 in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
-    };
-    auto store_scales = [&](const int64_t half) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < C::kScaleLoads; ++j)
-            xsl[half][(wave * C::kScaleLoads + j) * 64 + lane] = sv[j];
-        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));   // lgkmcnt(0)
     };
 
     const int wn = wave % C::WN, wm = wave / C::WN;
@@ -661,27 +661,49 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     auto rescale = [&](const i32x16 &acc, f32x16 &yv, float tb) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) yv[i] = fmaf((float)acc[i], tb, yv[i]);
+        // a use right here keeps machine sinking from moving the rescales past
+        // the next branch (which would keep all accumulators live at once)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(yv[i]));
     };
 
-    // One K block: sub-tiles in the order (a, b) = (0,0), (0,1), (1,0), ...;
-    // the rescale of each sub-tile is issued after the next sub-tile's MFMAs.
-    auto compute = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
-        i32x4 xf[SB][4];
+    // The first fragments of a K block (all activation fragments, the first
+    // weight fragments) and its scales.  They are read at the end of the
+    // previous block, between its last MFMAs and its last rescale, whose
+    // registers they reuse.
+    i32x4 xf[SB][4], wf0[4];
+    float xsv[SB], wsv;
+    auto read_first = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < SB; ++b) xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) wf0[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + frag_off[s]);
 #pragma unroll
         for (int b = 0; b < SB; ++b)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
-        // first W fragments, then the scales, all issued before the first wait
-        i32x4 wf0[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) wf0[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + frag_off[s]);
-        float xsv[SB];
-#pragma unroll
-        for (int b = 0; b < SB; ++b) xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
-        const float wsv = ws_cur;
-        ws_cur = ws_row[kb + 1 < KB ? kb + 1 : kb];   // next block's, issued a block ahead
-        __builtin_amdgcn_sched_barrier(0);
+        wsv = ws_cur;
+        ws_cur = ws_row[kb + 1 < KB ? kb + 1 : KB - 1];   // next block's, issued a block ahead
+    };
+    // Block kb + 1 is in LDS once this wave's fills have landed and every wave
+    // is past the barrier (which also ends every read of block kb): read its
+    // first fragments from `nxt`.  After the last block this reads stale LDS
+    // that nothing uses.
+    auto advance = [&](const char *nxt, int64_t kb) __attribute__((always_inline)) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        read_first(nxt, kb + 1);
+    };
+
+    // One K block: first the fills of block kb + 1 into the other stage (its
+    // previous block was finished before the last barrier; past the last
+    // block they read zeros), then the sub-tiles in the order (a, b) = (0,0),
+    // (0,1), (1,0), ...; the rescale of each sub-tile is issued after the next
+    // sub-tile's MFMAs, and the last one after the next block's first
+    // fragment reads.
+    auto compute = [&](const char *stage, char *nxt, int64_t kb) __attribute__((always_inline)) {
+        issue(nxt, kb + 1);
         float tb[SB];
 #pragma unroll
         for (int b = 0; b < SB; ++b) tb[b] = xsv[b] * wsv;
@@ -704,24 +726,25 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
                     const int pa = (j - 1) / SB, pb = (j - 1) % SB;
                     rescale(acc[(j - 1) & 1], y[pa][pb], tb[pb]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // the last sub-tile's MFMAs stay ahead of the barrier as well
+        asm volatile("" ::"v"(acc[(SA * SB - 1) & 1]));
+        advance(nxt, kb);
         rescale(acc[(SA * SB - 1) & 1], y[SA - 1][SB - 1], tb[SB - 1]);
     };
 
     issue(lds0, 0);
-    for (int64_t kb = 0; kb < KB; kb += 2) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    read_first(lds0, 0);
+    for (int64_t kb = 0;; kb += 2) {
         // block kb in lds0, block kb + 1 in lds1
-        wait_vmcnt<0>();
-        if ((kb & (C::kSB - 1)) == 0) store_scales((kb / C::kSB) & 1);
-        lds_barrier();
-        issue(lds1, kb + 1);
-        compute(lds0, kb);
+        compute(lds0, lds1, kb);
         if (kb + 1 >= KB) break;
-        wait_vmcnt<0>();
-        lds_barrier();
-        issue(lds0, kb + 2);
-        compute(lds1, kb + 1);
+        compute(lds1, lds0, kb + 1);
+        if (kb + 2 >= KB) break;
     }
     wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
 
