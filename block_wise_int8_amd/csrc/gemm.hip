@@ -119,11 +119,18 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
             wa[u][1] = as_i32x4(buf_load16(wr, in1 ? (uint32_t)(row * K + kk + 16) : kOobOffset));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
+                // lanes of token columns past M load nothing (zero operands)
                 const int64_t tok = mt * 16 + row;
-                xb[u][mt][0] = as_i32x4(buf_load16(xr, in0 ? (uint32_t)(tok * K + kk) : kOobOffset));
-                xb[u][mt][1] =
-                    as_i32x4(buf_load16(xr, in1 ? (uint32_t)(tok * K + kk + 16) : kOobOffset));
-                if constexpr (!PC) xsv[u][mt] = buf_load_f32(sr, ok ? (uint32_t)((tok * KB + b) * 4) : kOobOffset);
+                xb[u][mt][0] = i32x4{0, 0, 0, 0};
+                xb[u][mt][1] = i32x4{0, 0, 0, 0};
+                if constexpr (!PC) xsv[u][mt] = 0.f;
+                if (tok < p.M) {
+                    xb[u][mt][0] = as_i32x4(buf_load16(xr, in0 ? (uint32_t)(tok * K + kk) : kOobOffset));
+                    xb[u][mt][1] =
+                        as_i32x4(buf_load16(xr, in1 ? (uint32_t)(tok * K + kk + 16) : kOobOffset));
+                    if constexpr (!PC)
+                        xsv[u][mt] = buf_load_f32(sr, ok ? (uint32_t)((tok * KB + b) * 4) : kOobOffset);
+                }
             }
             if constexpr (!PC) wsv[u] = ws_row[ok ? b : KB - 1];
         }
