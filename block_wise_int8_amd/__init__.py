@@ -239,9 +239,12 @@ def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tensor | None = None,
-           y: torch.Tensor | None = None, block=(BLOCK, BLOCK)) -> torch.Tensor:
+           y: torch.Tensor | None = None, block=(BLOCK, BLOCK), xq: torch.Tensor | None = None,
+           xs: torch.Tensor | None = None) -> torch.Tensor:
     """Block-wise INT8 linear with dynamic activation scales -> bf16 [M, N]:
-    quant_act into scratch tensors, then gemm, through one C call."""
+    quant_act into the workspaces xq [M, K] int8 / xs [M, KB] fp32 (fresh
+    tensors when not given; they hold the quantised activations on return),
+    then gemm, through one C call."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype != torch.bfloat16:
         raise TypeError("x must be a 2-D bfloat16 tensor")
     if x.device.type != "cuda":
@@ -266,8 +269,16 @@ def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tenso
     _need(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError("y must be [M, N]")
-    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    xs = torch.empty((M, KB), dtype=torch.float32, device=x.device)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    _need(xq, "xq", torch.int8, 2)
+    if tuple(xq.shape) != (M, K):
+        raise ValueError("xq must be [%d, %d]" % (M, K))
+    if xs is None:
+        xs = torch.empty((M, KB), dtype=torch.float32, device=x.device)
+    _need(xs, "xs", torch.float32, 2)
+    if tuple(xs.shape) != (M, KB):
+        raise ValueError("xs must be [%d, %d]" % (M, KB))
     ldx = x.stride(0) if M > 1 else K
     _check(load().blockint8_linear(_ptr(x), ldx, _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K,
                                    block[0], block[1], _ptr(xq), _ptr(xs), _stream_handle(x.device)))

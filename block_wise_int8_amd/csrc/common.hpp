@@ -49,6 +49,45 @@ __device__ __forceinline__ int32_t quant_code(float x, float s, float r) {
     return (int32_t)q;
 }
 
+// Max over the 16 lanes of an aligned lane group (xor butterfly over lane
+// bits 0..3).  Every lane of the wave must execute it.
+__device__ __forceinline__ float group_max16(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+// One group of 128 activations spread over 16 lanes (8 bf16 per lane, in v):
+// the group scale s = amax / 127 (IEEE division) and the lane's 8 codes
+// (bytes of lo, hi in element order; all zero when s == 0).  Every lane of
+// the wave must execute it.
+__device__ __forceinline__ float quant_group16(const u32x4 &v, uint32_t &lo, uint32_t &hi) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = group_max16(amax);
+    const float s = amax / 127.0f;
+    lo = 0u;
+    hi = 0u;
+    if (s != 0.0f) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= ((uint32_t)quant_code(f[i], s, r) & 0xFFu) << (8 * i);
+            hi |= ((uint32_t)quant_code(f[4 + i], s, r) & 0xFFu) << (8 * i);
+        }
+    }
+    return s;
+}
+
 // Raw buffer resource over [base, base + num_bytes): loads at offsets past the
 // end return zero (gfx9 raw-buffer range check, stride 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {

@@ -126,14 +126,6 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(const int32_t 
     }
 }
 
-__device__ __forceinline__ float group_max16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
-    return v;
-}
-
 // silu(g) * u = g / (1 + exp(-g)) * u in fp32, the quotient through the
 // hardware reciprocal (within 1 ulp; the bf16 result then differs from the
 // correctly rounded quotient's only where the fp32 value sits at a bf16

@@ -23,15 +23,6 @@ namespace {
 
 constexpr int kQuantWaves = 4;          // waves per workgroup
 
-__device__ __forceinline__ float group_max16(float v) {
-    // xor-butterfly over the 16 lanes of a group (lanes differ in bits 0..3)
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
-    return v;
-}
-
 // rows (gather form, may be null): output row m quantises source row
 // rows[m] of x (src_rows rows); an index outside [0, src_rows) reads zeros.
 // kChunks: 16-byte loads in flight per lane (1 for small problems, where the
@@ -63,27 +54,9 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     for (int j = 0; j < kChunks; ++j) {
         const int64_t g = g0 + 4 * j, k = g * kBlock + (lane & 15) * 8;
         const bool valid = (g < KB) && (k < K);
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = bf16_bits_to_f32(v[j][i] & 0xFFFFu);
-            f[2 * i + 1] = bf16_bits_to_f32(v[j][i] >> 16);
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = group_max16(amax);
-        const float s = amax / 127.0f;
+        uint32_t lo, hi;
+        const float s = quant_group16(v[j], lo, hi);
         if (!valid) continue;
-        uint32_t lo = 0u, hi = 0u;
-        if (s != 0.0f) {
-            const float r = 1.0f / s;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lo |= ((uint32_t)quant_code(f[i], s, r) & 0xFFu) << (8 * i);
-                hi |= ((uint32_t)quant_code(f[4 + i], s, r) & 0xFFu) << (8 * i);
-            }
-        }
         *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
         if ((lane & 15) == 0) xs[m * KB + g] = s;
     }

@@ -246,6 +246,25 @@ def test_linear_equals_quant_then_gemm(M, N, K, ldx):
         assert_gemm_close(y_one, oracle.gemm(q_ref, s_ref, w, ws, bias=b), "linear M=%d" % M)
 
 
+def test_linear_workspaces_hold_the_codes():
+    """Caller-given workspaces hold the quantised activations on return."""
+    M, N, K = 8, 512, 1040
+    x, w, ws = make_case(77, M, N, K)
+    KB = (K + 127) // 128
+    xq = torch.empty((M, K), dtype=torch.int8, device=device())
+    xs = torch.empty((M, KB), dtype=torch.float32, device=device())
+    wd, wsd = to_dev(w), to_dev(ws)
+    y = bi8.linear(bf16_to_dev(x), wd, wsd, xq=xq, xs=xs)
+    q_ref, s_ref = oracle.quant_act(x)
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert_gemm_close(bf16_bits(y), oracle.gemm(q_ref, s_ref, w, ws), "linear with workspaces")
+    with pytest.raises(ValueError):
+        bi8.linear(bf16_to_dev(x), wd, wsd, xq=xq[:, :16])
+    with pytest.raises(ValueError):
+        bi8.linear(bf16_to_dev(x), wd, wsd, xs=xs[:, :2])
+
+
 def test_gemm_unaligned_output_rows():
     """N % 4 != 0 takes the element-wise store path."""
     M, N, K = 70, 333, 256
