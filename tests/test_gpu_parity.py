@@ -246,6 +246,33 @@ def test_linear_equals_quant_then_gemm(M, N, K, ldx):
         assert_gemm_close(y_one, oracle.gemm(q_ref, s_ref, w, ws, bias=b), "linear M=%d" % M)
 
 
+@pytest.fixture(scope="module")
+def max_k_case():
+    """K = 2^23, the largest K the C ABI accepts: a 256-row weight tile is then
+    exactly 2^31 bytes, the largest buffer range a kernel addresses."""
+    M, N, K = 40, 256, 1 << 23
+    rng = wl.rng_for((1 << 23, 1))
+    x = wl.activations(rng, M, K)
+    w = wl.weights(rng, N, K)
+    ws = wl.weight_scales(rng, *oracle.scale_shape(N, K))
+    xq, xs = bi8.quant_act(bf16_to_dev(x))
+    yield x, w, ws, xq, xs, to_dev(w), to_dev(ws)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant,rows", [
+    (bi8.GEMM_SKINNY, 8), (bi8.GEMM_TILE_128X64, 40), (bi8.GEMM_TILE_256X128, 40), (bi8.GEMM_TILE_256X256, 40),
+])
+def test_gemm_at_max_k_every_kernel(max_k_case, variant, rows):
+    x, w, ws, xq, xs, wd, wsd = max_k_case
+    y = bf16_bits(bi8.gemm(xq[:rows], xs[:rows], wd, wsd, variant=variant))
+    q_ref, s_ref = oracle.quant_act(x[rows - 1:rows])
+    # the codes of the sampled row are bit-exact, and its outputs within tolerance
+    assert np.array_equal(xq[rows - 1:rows].cpu().numpy(), q_ref)
+    assert np.array_equal(xs[rows - 1:rows].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert_gemm_close(y[rows - 1:rows], oracle.gemm(q_ref, s_ref, w, ws), "K = 2^23, variant %d" % variant)
+
+
 def test_linear_workspaces_hold_the_codes():
     """Caller-given workspaces hold the quantised activations on return."""
     M, N, K = 8, 512, 1040

@@ -64,3 +64,22 @@ def test_per_channel_linear_and_bias():
     y = bf16_bits(bi8.linear(bf16_to_dev(x), to_dev(w), to_dev(ws), bias=bf16_to_dev(bias), block=(1, K)))
     xq, xs = oracle.quant_act(x, block_k=K)
     assert_gemm_close(y, oracle.gemm(xq, xs, w, ws, bias=bias, block=(1, K)), "per-channel linear")
+
+
+@pytest.mark.parametrize("M", [8, 40])
+def test_per_channel_max_k_saturated_sums_bit_exact(M):
+    """K = 2^17, the per-channel limit, with every code at +-127: a row's int32
+    sum reaches +-127^2 * 2^17 = +-2114060288, just inside int32 (M = 8 runs
+    the skinny kernel, M = 40 the tiled one).  All partial sums are exact in
+    fp32 here, so y must equal the oracle bit for bit."""
+    N, K = 64, 1 << 17
+    xq = np.full((M, K), 127, np.int8)
+    xq[1::2] = -127
+    w = np.full((N, K), 127, np.int8)
+    w[::3] = -127
+    xs = np.ones((M, 1), np.float32)
+    ws = np.ones((N, 1), np.float32)
+    y = bf16_bits(bi8.gemm(to_dev(xq), to_dev(xs), to_dev(w), to_dev(ws), block=(1, K)))
+    y_ref = oracle.gemm(xq, xs, w, ws, block=(1, K))
+    assert abs(int(xq[0].astype(np.int64) @ w[1].astype(np.int64))) == 127 * 127 * K
+    assert np.array_equal(y, y_ref)
