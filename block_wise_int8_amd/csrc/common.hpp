@@ -36,11 +36,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // One int8 code clamp(rne(x / s), -127, 127) with x / s the IEEE correctly
-// rounded quotient, computed from r = 1 / s (correctly rounded) by a single
-// multiply.  y = x * r is within |x / s| * 1.5 * 2^-23 <= 2.3e-5 of fl(x / s)
-// for |x / s| <= 127.5, so the two round to the same integer unless y lies
-// within 2^-14 of a half-integer; those products (and non-finite ones, e.g.
-// r = inf for a subnormal s) take the division.
+// rounded quotient, computed from r = rcp(s), the hardware reciprocal (within
+// 1 ulp of 1 / s), by a single multiply.  y = x * r is then within
+// |x / s| * 2^-22 <= 3.1e-5 of fl(x / s) for |x / s| <= 127.5, so the two
+// round to the same integer unless y lies within 2^-14 of a half-integer;
+// those products (and non-finite ones, e.g. r = inf for a subnormal s) take
+// the division.
 __device__ __forceinline__ int32_t quant_code(float x, float s, float r) {
     const float y = x * r;
     float q = rintf(y);
@@ -78,7 +79,7 @@ __device__ __forceinline__ float quant_group16(const u32x4 &v, uint32_t &lo, uin
     lo = 0u;
     hi = 0u;
     if (s != 0.0f) {
-        const float r = 1.0f / s;
+        const float r = __builtin_amdgcn_rcpf(s);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             lo |= ((uint32_t)quant_code(f[i], s, r) & 0xFFu) << (8 * i);

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kSiluWaves * 64) void silu_mul_quant_kernel(
         if (!valid) continue;
         uint32_t lo = 0u, hi = 0u;
         if (s != 0.0f) {
-            const float rs = 1.0f / s;
+            const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 lo |= ((uint32_t)quant_code(a[j], s, rs) & 0xFFu) << (8 * j);

@@ -12,8 +12,9 @@
 // problems, 8 groups in two halves with both loads in flight before either is
 // used.  The group max is reduced across the 16 lanes with cross-lane moves.  The
 // scale is an IEEE correctly rounded division and denormals are kept (build
-// flags); codes come from one multiply by 1 / s with the division taken where
-// the two could round apart (quant_code), so codes and scales are bit-exact.
+// flags); codes come from one multiply by the hardware reciprocal of s, with
+// the division taken wherever the two could round apart (quant_code), so
+// codes and scales are bit-exact.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t *__res
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = amax / 127.0f;
-    const float r = 1.0f / s;
+    const float r = __builtin_amdgcn_rcpf(s);
     if (t == 0) ws[bn * KB + bk] = s;
     if (!row_ok) return;
 #pragma unroll
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const float s = amax / 127.0f;
-    const float r = 1.0f / s;
+    const float r = __builtin_amdgcn_rcpf(s);
     if (t == 0) xs[m] = s;
     for (int64_t k = 8 * t; k < K; k += 8 * 256) {
         uint32_t lo = 0u, hi = 0u;

@@ -74,11 +74,8 @@ def test_quant_special_values_bit_exact():
     assert 0 < s[4, 0] < np.finfo(np.float32).tiny
 
 
-@pytest.mark.parametrize("amax_bits", [0x3F80, 0x4040, 0x42C8, 0x42FE, 0x3E9A, 0x0380, 0x0001, 0x7F7F])
-def test_quant_every_bf16_below_amax_bit_exact(amax_bits):
-    """Every bf16 value of magnitude <= amax, 127 per group with amax itself first:
-    covers each quotient x / s the group can produce, ties and near-ties included
-    (amax 1, 3, 100, 127, 0.3, 2^-120, the smallest subnormal, the largest finite)."""
+def groups_below(amax_bits):
+    """Every bf16 value of magnitude <= amax, 127 per group with amax itself first."""
     b = np.arange(0, 0x7F80, dtype=np.uint32)          # every finite non-negative bf16
     vals = b[b <= amax_bits]
     vals = np.concatenate([vals, vals | 0x8000]).astype(np.uint16)
@@ -88,10 +85,35 @@ def test_quant_every_bf16_below_amax_bit_exact(amax_bits):
     flat = x[:, 1:].reshape(-1)
     flat[:len(vals)] = vals
     x[:, 1:] = flat.reshape(n, 127)
+    return x
+
+
+@pytest.mark.parametrize("amax_bits", [0x3F80, 0x4040, 0x42C8, 0x42FE, 0x3E9A, 0x0380, 0x0001, 0x7F7F])
+def test_quant_every_bf16_below_amax_bit_exact(amax_bits):
+    """Covers each quotient x / s the group can produce, ties and near-ties included
+    (amax 1, 3, 100, 127, 0.3, 2^-120, the smallest subnormal, the largest finite)."""
+    x = groups_below(amax_bits)
     q_ref, s_ref = oracle.quant_act(x)
     q, s = gpu_quant(x)
     assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(q, q_ref)
+
+
+def test_quant_every_bf16_for_every_mantissa_of_amax_bit_exact():
+    """The codes are multiplies by the hardware reciprocal of s (within 1 ulp),
+    with the division wherever the product comes within 2^-14 of a half-integer.
+    For normal values, scaling amax and x by a power of two scales s and every
+    quotient exactly, so amax in [1, 2) at each of its 128 bf16 mantissas covers
+    the normal range. The 127 subnormal maxima (s subnormal, reciprocal
+    overflowing) and the 128 largest (smallest normal reciprocals) cover the
+    ends. Every bf16 input of magnitude <= amax for each: ~13 M codes."""
+    maxima = list(range(0x3F80, 0x4000)) + list(range(0x0001, 0x0080)) + list(range(0x7F00, 0x7F80))
+    x = np.concatenate([groups_below(a) for a in maxima])
+    q_ref, s_ref = oracle.quant_act(x)
+    q, s = gpu_quant(x)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    bad = np.nonzero(np.any(q != q_ref, axis=1))[0]
+    assert bad.size == 0, "groups with differing codes: %d (first amax bits %#06x)" % (bad.size, x[bad[0], 0])
 
 
 @pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (5, 144), (7, 4000), (64, 128), (2, 14336),
