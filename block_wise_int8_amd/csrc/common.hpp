@@ -35,6 +35,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
+// Two fp32 values to packed bf16 bits (lo in bits 0..15) by the hardware
+// conversion: round to nearest even, as f32_to_bf16_bits, except that a NaN
+// keeps an unspecified quiet-NaN pattern.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // One int8 code clamp(rne(x / s), -127, 127) with x / s the IEEE correctly
 // rounded quotient, computed from r = rcp(s), the hardware reciprocal (within
 // 1 ulp of 1 / s), by a single multiply.  y = x * r is then within

@@ -173,13 +173,14 @@ __global__ __launch_bounds__(kSiluWaves * 64) void silu_mul_quant_kernel(
         const int64_t g = g0 + 4 * c, i = g * kBlock + (lane & 15) * 8;
         const bool valid = g < IB && i < I;
         float a[8];
-        uint32_t ab[8];
+        uint32_t ab2[4];   // the bf16 activation, two per word
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t gb = (j & 1) ? (gv[c][j >> 1] >> 16) : (gv[c][j >> 1] & 0xFFFFu);
-            const uint32_t ub = (j & 1) ? (uv[c][j >> 1] >> 16) : (uv[c][j >> 1] & 0xFFFFu);
-            ab[j] = f32_to_bf16_bits(silu_times(bf16_bits_to_f32(gb), bf16_bits_to_f32(ub)));
-            a[j] = bf16_bits_to_f32(ab[j]);
+        for (int j = 0; j < 4; ++j) {
+            const float s0 = silu_times(bf16_bits_to_f32(gv[c][j] & 0xFFFFu), bf16_bits_to_f32(uv[c][j] & 0xFFFFu));
+            const float s1 = silu_times(bf16_bits_to_f32(gv[c][j] >> 16), bf16_bits_to_f32(uv[c][j] >> 16));
+            ab2[j] = f32x2_to_bf16x2_bits(s0, s1);
+            a[2 * j] = bf16_bits_to_f32(ab2[j] & 0xFFFFu);
+            a[2 * j + 1] = bf16_bits_to_f32(ab2[j] >> 16);
         }
         float amax = 0.0f;
 #pragma unroll
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(kSiluWaves * 64) void silu_mul_quant_kernel(
         if (a_out) {
             u32x4 o;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = ab[2 * j] | (ab[2 * j + 1] << 16);
+            for (int j = 0; j < 4; ++j) o[j] = ab2[j];
             *reinterpret_cast<u32x4 *>(a_out + r * I + i) = o;
         }
     }

@@ -263,7 +263,8 @@ int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, co
  *   a[r, i] = bf16( silu(gate) * up ),  silu(z) = z / (1 + exp(-z))  (fp32;
  *             exp and the quotient through the hardware exp2 and
  *             reciprocal, so a may differ from a correctly rounded
- *             evaluation by one bf16 ulp in rare cases)
+ *             evaluation by one bf16 ulp in rare cases; the bf16 rounding is
+ *             to nearest even, a NaN keeps an unspecified NaN pattern)
  *   aq, as  = blockint8_quant_act(a)   (bit for bit, on this a)
  *
  *   h   bf16 [R, 2I] (16-byte aligned)   aq int8 [R, I]   as fp32 [R, ceil(I/128)]
