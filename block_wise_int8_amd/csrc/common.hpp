@@ -59,13 +59,22 @@ __device__ __forceinline__ int32_t quant_code(float x, float s, float r) {
     return (int32_t)q;
 }
 
-// Max over the 16 lanes of an aligned lane group (xor butterfly over lane
-// bits 0..3).  Every lane of the wave must execute it.
+// v from the lane n places lower in its row of 16 lanes, cyclically (DPP
+// row_ror:n, a register-to-register move; n in 1..15).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    static_assert(N >= 1 && N <= 15, "row_ror range");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Max over the 16 lanes of an aligned lane group (a row of the wave): after
+// rotations by 1, 2, 4 and 8 every lane holds the max of a cyclic window of
+// 16, i.e. of the whole row.  Every lane of the wave must execute it.
 __device__ __forceinline__ float group_max16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, row_ror<1>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<8>(v));
     return v;
 }
 
