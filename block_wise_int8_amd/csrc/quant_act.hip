@@ -105,10 +105,13 @@ namespace bi8 {
 
 namespace {
 
+// Max over the 64 lanes of the wave: the row maxima by DPP rotations, then
+// the four rows' by lane reads (uniform result).
 __device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+    v = group_max16(v);
+    const int b = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 __global__ __launch_bounds__(256) void quant_weight_kernel(const uint16_t *__restrict__ w, int64_t N, int64_t K,
@@ -173,11 +176,16 @@ hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t 
 
 // Per-token quantisation (the per-channel form: one group spanning all K):
 // one workgroup of 256 threads per row, two passes over the row (max, then
-// codes), 16-byte loads.  Same arithmetic as the 128-group kernel.
+// codes), 16-byte loads; a row of up to 8192 entries is read once and kept in
+// registers for the second pass.  Same arithmetic as the 128-group kernel.
 namespace bi8 {
 
 namespace {
 
+// kChunks > 0: the row fits in kChunks 16-byte loads per thread (K <=
+// 2048 kChunks), which stay in registers between the two passes; 0: the
+// second pass reads the row again.
+template <int kChunks>
 __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__restrict__ x, int64_t K,
                                                               int64_t ldx, int8_t *__restrict__ xq,
                                                               float *__restrict__ xs) {
@@ -185,12 +193,24 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
     const int t = threadIdx.x;
     const int64_t m = blockIdx.x;
     const uint16_t *row = x + m * ldx;
+    u32x4 v[kChunks > 0 ? kChunks : 1];
     float amax = 0.0f;
-    for (int64_t k = 8 * t; k < K; k += 8 * 256) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+    auto row_max = [&](const u32x4 &c) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)), fabsf(bf16_bits_to_f32(v[j] >> 16))));
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(c[j] & 0xFFFFu)), fabsf(bf16_bits_to_f32(c[j] >> 16))));
+    };
+    if constexpr (kChunks > 0) {
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int64_t k = 8 * (t + 256 * c);
+            v[c] = u32x4{0u, 0u, 0u, 0u};
+            if (k < K) v[c] = *reinterpret_cast<const u32x4 *>(row + k);
+        }
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) row_max(v[c]);
+    } else {
+        for (int64_t k = 8 * t; k < K; k += 8 * 256) row_max(*reinterpret_cast<const u32x4 *>(row + k));
     }
     amax = wave_max64(amax);
     if ((t & 63) == 0) wmax[t >> 6] = amax;
@@ -199,19 +219,27 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
     const float s = amax / 127.0f;
     const float r = __builtin_amdgcn_rcpf(s);
     if (t == 0) xs[m] = s;
-    for (int64_t k = 8 * t; k < K; k += 8 * 256) {
+    auto codes = [&](const u32x4 &c, int64_t k) __attribute__((always_inline)) {
         uint32_t lo = 0u, hi = 0u;
         if (s != 0.0f) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                lo |= ((uint32_t)quant_code(bf16_bits_to_f32(v[j] & 0xFFFFu), s, r) & 0xFFu) << (16 * j);
-                lo |= ((uint32_t)quant_code(bf16_bits_to_f32(v[j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
-                hi |= ((uint32_t)quant_code(bf16_bits_to_f32(v[2 + j] & 0xFFFFu), s, r) & 0xFFu) << (16 * j);
-                hi |= ((uint32_t)quant_code(bf16_bits_to_f32(v[2 + j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
+                lo |= ((uint32_t)quant_code(bf16_bits_to_f32(c[j] & 0xFFFFu), s, r) & 0xFFu) << (16 * j);
+                lo |= ((uint32_t)quant_code(bf16_bits_to_f32(c[j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
+                hi |= ((uint32_t)quant_code(bf16_bits_to_f32(c[2 + j] & 0xFFFFu), s, r) & 0xFFu) << (16 * j);
+                hi |= ((uint32_t)quant_code(bf16_bits_to_f32(c[2 + j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
             }
         }
         *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
+    };
+    if constexpr (kChunks > 0) {
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int64_t k = 8 * (t + 256 * c);
+            if (k < K) codes(v[c], k);
+        }
+    } else {
+        for (int64_t k = 8 * t; k < K; k += 8 * 256) codes(*reinterpret_cast<const u32x4 *>(row + k), k);
     }
 }
 
@@ -221,7 +249,15 @@ hipError_t launch_quant_act_per_token(const uint16_t *x, int64_t M, int64_t K, i
                                       float *xs, hipStream_t stream) {
     if (M == 0) return hipSuccess;
     if (M > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_act_token_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+    const int64_t chunks = (K + 2047) / 2048;   // 16-byte loads per thread
+    if (chunks <= 1)
+        hipLaunchKernelGGL((quant_act_token_kernel<1>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+    else if (chunks <= 2)
+        hipLaunchKernelGGL((quant_act_token_kernel<2>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+    else if (chunks <= 4)
+        hipLaunchKernelGGL((quant_act_token_kernel<4>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+    else
+        hipLaunchKernelGGL((quant_act_token_kernel<0>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
     return hipGetLastError();
 }
 
