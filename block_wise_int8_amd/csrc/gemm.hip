@@ -927,6 +927,148 @@ __global__ __launch_bounds__(512) void gemm_perch_kernel(GemmArgs p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// Per-channel, 256 x 256 tiles: the wide kernel's tile, wave grid (8 waves of
+// 128 weight rows x 64 activation rows), 2-stage LDS ring and swizzle, with no
+// per-block scale at all.  Each of a wave's 8 sub-tiles keeps one int32
+// accumulator over the whole of K (8 x 16 registers), so a K block is just
+// its fragment reads and 32 MFMAs; the fp32 scales multiply once, in the
+// store.  For problems with enough 256 x 256 tiles to fill the chip.
+__global__ __launch_bounds__(WideCfg::kThreads) void gemm_perch_wide_kernel(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = WideCfg;
+    constexpr int SA = C::SA, SB = C::SB;
+    __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
+
+    Tile t;
+    if (!decode_tile<C::kBN, C::kBM, false, kGroupMWide>(p, t)) return;
+    if (t.rows <= 0) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t K = p.K, KB = p.KB;
+    const int64_t wrows = p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
+
+    // load pieces as in the wide kernel: one chunk per lane, piece j of a
+    // lane j * 64 rows below piece 0
+    const int r_in = lane >> 3;
+    const int chunk = 16 * ((lane & 7) ^ r_in ^ (wave & 1));
+    const uint32_t go = (uint32_t)((8 * wave + r_in) * K + chunk);
+    const uint32_t piece_stride = (uint32_t)(8 * C::kWaves * K);
+    const int kb_in = (int)((K - chunk + kBlock - 1) / kBlock);   // kb < kb_in <=> kb * 128 + chunk < K
+    auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
+        const uint32_t kofs = (uint32_t)kb * kBlock;
+        const bool in_k = (int)kb < kb_in;
+#pragma unroll
+        for (int j = 0; j < C::kWLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024), 16,
+                in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::kXLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
+                in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
+    };
+
+    const int wn = wave % C::WN, wm = wave / C::WN;
+    const int rr = lane & 31, hi = lane >> 5;
+    const int swz = (rr & 7) ^ ((rr >> 3) & 1);
+    int frag_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
+    const int wrow0 = (wn * C::kWaveN + rr) * 128;
+    const int xrow0 = C::kXOff + (wm * C::kWaveM + rr) * 128;
+
+    i32x16 acc[SA][SB];
+#pragma unroll
+    for (int a = 0; a < SA; ++a)
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0;
+    auto compute = [&](const char *stage) __attribute__((always_inline)) {
+        i32x4 xf[SB][4];
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
+#pragma unroll
+        for (int a = 0; a < SA; ++a) {
+            i32x4 wf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                wf[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int b = 0; b < SB; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[s], xf[b][s], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // block kb in lds[kb % 2]: after this wave's fills of block kb have landed
+    // and every wave is past the barrier (so done with block kb - 1), block
+    // kb + 1 starts filling the other stage
+    issue(lds0, 0);
+    int64_t kb = 0;
+    for (; kb + 1 < KB; kb += 2) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        issue(lds1, kb + 1);
+        compute(lds0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        issue(lds0, kb + 2);
+        compute(lds1);
+    }
+    if (kb < KB) {   // odd block count: the last block sits in lds0
+        wait_vmcnt<0>();
+        lds_barrier();
+        compute(lds0);
+    }
+    wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
+
+    // Store: lane -> token column rr; element i -> weight row 8 (i / 4) + 4 hi + i % 4.
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+        const int64_t ml = wm * C::kWaveM + b * 32 + rr;
+        if (ml >= t.rows) continue;
+        const float xsv = p.xs[t.m0 + ml];
+        uint16_t *yrow = p.y + (t.m0 + ml) * p.N;
+#pragma unroll
+        for (int a = 0; a < SA; ++a) {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int64_t n = t.n0 + wn * C::kWaveN + a * 32 + 8 * i4 + 4 * hi;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float wsv = n + e < p.N ? t.ws[n + e] : 0.0f;
+                    v[e] = (float)acc[a][b][4 * i4 + e] * (xsv * wsv);
+                    if (p.bias && n + e < p.N) v[e] += bf16_bits_to_f32(p.bias[n + e]);
+                }
+                if (p.wide_store) {
+                    if (n < p.N) {
+                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                }
+            }
+        }
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 // Explicit instantiations: the host pass must emit a launch stub for every
 // variant launched below.
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true>(GemmArgs);
@@ -1051,6 +1193,15 @@ hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8
         else
             hipLaunchKernelGGL((gemm_skinny_kernel<2, true>), dim3((unsigned)tiles), dim3(kSkinnyWaves * 64), 0,
                                stream, p, bpw);
+        return hipGetLastError();
+    }
+    if (((M + 255) / 256) * ((N + 255) / 256) >= 256) {
+        // enough 256 x 256 tiles to fill the chip
+        p.tiles_m = (M + 255) / 256;
+        p.tiles_n = (N + 255) / 256;
+        const int64_t total = p.tiles_m * p.tiles_n;
+        if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(gemm_perch_wide_kernel, dim3((unsigned)total), dim3(WideCfg::kThreads), 0, stream, p);
         return hipGetLastError();
     }
     p.tiles_m = (M + 127) / 128;

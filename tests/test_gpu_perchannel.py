@@ -36,7 +36,7 @@ def pc_case(seed, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (8, 4096, 4096), (200, 1000, 1040), (513, 520, 4000),
-                                   (4096, 4096, 4096), (33, 7, 16)])
+                                   (4096, 4096, 4096), (33, 7, 16), (4000, 4100, 1040)])
 def test_per_channel_gemm_vs_oracle(M, N, K):
     x, w, ws = pc_case((M, N, K, 1), M, N, K)
     xq, xs = oracle.quant_act(x, block_k=K)
@@ -46,12 +46,16 @@ def test_per_channel_gemm_vs_oracle(M, N, K):
     assert_gemm_close(y[rows], y_ref, "per-channel M=%d N=%d K=%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 300, 1040), (130, 64, 528)])
+@pytest.mark.parametrize("M,N,K", [(40, 300, 1040), (130, 64, 528), (1300, 11002, 272)])
 def test_per_channel_integer_closed_form_bit_exact(M, N, K):
+    """Unit scales: y is the integer product rounded once to bf16.  The sums
+    stay below 127^2 * K < 2^53, so the float64 product is exact.  The last
+    shape has 6 x 43 tiles of 256 x 256, an odd count of 128-wide K blocks
+    with a ragged tail, and an N that rules out 4-wide stores."""
     rng = np.random.default_rng(M * N)
     xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
     w = wl.weights(rng, N, K)
-    exact = (xq.astype(np.int64) @ w.astype(np.int64).T).astype(np.float32)
+    exact = (xq.astype(np.float64) @ w.astype(np.float64).T).astype(np.float32)
     y = bf16_bits(bi8.gemm(to_dev(xq), to_dev(np.ones((M, 1), np.float32)), to_dev(w),
                            to_dev(np.ones((N, 1), np.float32)), block=(1, K)))
     assert np.array_equal(y, wl.to_bf16_bits(exact))
@@ -83,3 +87,20 @@ def test_per_channel_max_k_saturated_sums_bit_exact(M):
     y_ref = oracle.gemm(xq, xs, w, ws, block=(1, K))
     assert abs(int(xq[0].astype(np.int64) @ w[1].astype(np.int64))) == 127 * 127 * K
     assert np.array_equal(y, y_ref)
+
+
+def test_per_channel_max_k_saturated_sums_many_tiles():
+    """K = 2^17 with every code at +-127 on 16 x 16 tiles of 256 x 256: each
+    output is +-127^2 * 2^17 exactly, with the sign of its token row times
+    the sign of its weight row."""
+    M = N = 4096
+    K = 1 << 17
+    sm = np.where(np.arange(M) % 2 == 1, -1, 1).astype(np.int8)
+    sn = np.where(np.arange(N) % 3 == 0, -1, 1).astype(np.int8)
+    xq = np.repeat((127 * sm)[:, None], K, axis=1)
+    w = np.repeat((127 * sn)[:, None], K, axis=1)
+    y = bf16_bits(bi8.gemm(to_dev(xq), to_dev(np.ones((M, 1), np.float32)), to_dev(w),
+                           to_dev(np.ones((N, 1), np.float32)), block=(1, K)))
+    del xq, w
+    exact = np.outer(sm.astype(np.float32), sn.astype(np.float32)) * np.float32(127 * 127 * K)
+    assert np.array_equal(y, wl.to_bf16_bits(exact))
