@@ -277,16 +277,27 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
 // barriers; between them one group issues its MFMAs while the other converts
 // and rescales its previous block (VALU), so each SIMD keeps its matrix core
 // and its vector ALU busy at the same time.
-template <int WN, int WM, int SA, int SB, bool MOE, bool PING>
+template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS>
 __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     // (device pass only: the body's address-space casts are not valid host
     // code, and the host pass only needs the launch stub)
     using C = TileCfg<WN, WM, SA, SB>;
     static_assert(!PING || (WM == 2 && WN == 4), "ping-pong pairs waves w and w + 4 on one SIMD");
+    // the ring: NS stages, loads NS - 1 blocks ahead; a scale batch (kSB
+    // blocks) must be published before the next one's loads are issued
+    static_assert(NS >= 3 && NS <= 6 && NS - 2 < C::kSB, "ring depth");
+    // one array per stage: with a separate object per stage the compiler
+    // knows which in-flight fills a fragment read cannot alias
     __shared__ __attribute__((aligned(1024))) char lds0[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds2[C::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds3[NS > 3 ? C::kStageBytes : 1];
+    __shared__ __attribute__((aligned(1024))) char lds4[NS > 4 ? C::kStageBytes : 1];
+    __shared__ __attribute__((aligned(1024))) char lds5[NS > 5 ? C::kStageBytes : 1];
+    auto lds = [&](const int i) __attribute__((always_inline)) -> char * {
+        return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : i == 3 ? lds3 : i == 4 ? lds4 : lds5;
+    };
     __shared__ float xsl[2][C::kBM * C::kSB];   // activation-scale batches, double-buffered
 
     Tile t;
@@ -451,22 +462,23 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
             for (int b = 0; b < SB; ++b) asm volatile("" : "+v"(y[a][b]));
     };
-    // Before step kb, only block kb + 1's loads may still be in flight (plus
-    // its scale batch when block kb + 1 starts one).
+    // Before step kb, only the loads of blocks kb + 1 .. kb + NS - 2 may still
+    // be in flight, plus the scale batch of the one of them that starts a
+    // batch (at most one does: NS - 2 < kSB).
     auto wait_stage = [&](int64_t kb) __attribute__((always_inline)) {
-        if (((kb + 1) & (C::kSB - 1)) == 0)
-            wait_vmcnt<C::kTileLoads + C::kScaleLoads>();
+        if ((int)(kb & (C::kSB - 1)) >= C::kSB - (NS - 2))
+            wait_vmcnt<(NS - 2) * C::kTileLoads + C::kScaleLoads>();
         else
-            wait_vmcnt<C::kTileLoads>();
+            wait_vmcnt<(NS - 2) * C::kTileLoads>();
     };
 
-    // 3-stage ring: block kb lives in lds[kb % 3]; loads run two blocks ahead.
-    // Before the first barrier of step kb, this wave's loads of block kb are
-    // complete (only block kb + 1's are still in flight).
+    // NS-stage ring: block kb lives in lds[kb % NS]; loads run NS - 1 blocks
+    // ahead.  Before the first barrier of step kb, this wave's loads of block
+    // kb are complete.
     auto step = [&](const int group, char *cur, char *ahead, int64_t kb) __attribute__((always_inline)) {
         wait_stage(kb);
         lds_barrier();
-        issue(ahead, kb + 2);
+        issue(ahead, kb + NS - 1);
         if (!PING || group == 0) {
             mma(cur, kb);
             if (PING) lds_barrier();
@@ -481,17 +493,17 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
         if (((kb + 1) & (C::kSB - 1)) == 0) store_scales(((kb + 1) / C::kSB) & 1);
     };
     auto run = [&](const int group) __attribute__((always_inline)) {
-        issue(lds0, 0);
-        issue(lds1, 1);
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i) issue(lds(i), i);
         store_scales(0);
         int64_t kb = 0;
-        for (; kb + 3 <= KB; kb += 3) {
-            step(group, lds0, lds2, kb);
-            step(group, lds1, lds0, kb + 1);
-            step(group, lds2, lds1, kb + 2);
+        for (; kb + NS <= KB; kb += NS) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) step(group, lds(i), lds((i + NS - 1) % NS), kb + i);
         }
-        if (kb < KB) step(group, lds0, lds2, kb++);
-        if (kb < KB) step(group, lds1, lds0, kb++);
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (kb < KB) step(group, lds(i), lds((i + NS - 1) % NS), kb++);
         if (PING && group == 1) epi();   // the last block
     };
     if (!PING || wm == 0)
@@ -1071,20 +1083,21 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_perch_wide_kernel(Gemm
 
 // Explicit instantiations: the host pass must emit a launch stub for every
 // variant launched below.
-template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true, 3>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true, 3>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 4>(GemmArgs);
 template __global__ void gemm_wide_kernel<false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true>(GemmArgs);
 
-template <int WN, int WM, int SA, int SB, bool MOE, bool PING>
+template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS>
 hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
     using C = TileCfg<WN, WM, SA, SB>;
     const int64_t total = p.tiles_m * p.tiles_n;
     if (total <= 0) return hipSuccess;
     if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, SA, SB, MOE, PING>), dim3((unsigned)total), dim3(C::kThreads),
+    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, SA, SB, MOE, PING, NS>), dim3((unsigned)total), dim3(C::kThreads),
                        0, stream, p);
     return hipGetLastError();
 }
@@ -1168,11 +1181,15 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
         case GemmPath::kTile256x128:
             p.tiles_m = (M + 127) / 128;
             p.tiles_n = (N + 255) / 256;
-            return launch_tiled<4, 2, 2, 2, false, true>(p, stream);
+            return launch_tiled<4, 2, 2, 2, false, true, 3>(p, stream);
         case GemmPath::kTile128x64:
             p.tiles_m = (M + 63) / 64;
             p.tiles_n = (N + 127) / 128;
-            return launch_tiled<4, 2, 1, 1, false, true>(p, stream);
+            // A grid that leaves CUs idle runs one workgroup per CU: a fourth
+            // stage (96 KB of LDS) lets the loads run a block further ahead.
+            // A larger grid keeps the 72 KB ring, two workgroups per CU.
+            if (p.tiles_m * p.tiles_n <= 256) return launch_tiled<4, 2, 1, 1, false, true, 4>(p, stream);
+            return launch_tiled<4, 2, 1, 1, false, true, 3>(p, stream);
         default:
             return hipErrorInvalidValue;
     }
@@ -1228,7 +1245,7 @@ hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, con
         case GemmPath::kTile256x128:
             p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
             p.tiles_n = (N + 255) / 256;
-            return launch_tiled<4, 2, 2, 2, true, true>(p, stream);
+            return launch_tiled<4, 2, 2, 2, true, true, 3>(p, stream);
         default:
             return hipErrorInvalidValue;
     }

@@ -172,8 +172,12 @@ def test_gemm_shapes_vs_oracle(M, N, K):
 
 
 # Shapes spanning several tiles of every tiled kernel, with ragged M, N and K
-# tails, including a tile row with a single valid activation row.
-@pytest.mark.parametrize("M,N,K", [(513, 520, 1040), (769, 1000, 400), (257, 2056, 272)])
+# tails, including a tile row with a single valid activation row.  The 128 x 64
+# kernel runs a 4-stage ring on grids of at most 256 tiles and a 3-stage ring
+# on larger ones (the last two shapes: 336 and 342 tiles, with 25 and 11 K
+# blocks, so both leave a partial turn of the ring).
+@pytest.mark.parametrize("M,N,K", [(513, 520, 1040), (769, 1000, 400), (257, 2056, 272),
+                                   (1000, 2600, 3088), (1100, 2400, 1296)])
 def test_gemm_tiled_variants_multi_tile(M, N, K):
     x, w, ws = make_case((M, N, K, 7), M, N, K)
     xq, xs = oracle.quant_act(x)
