@@ -155,8 +155,8 @@ int32_t blockint8_gemm_variant(int32_t variant, const int8_t *xq, const float *x
     const bool pc = per_channel(block_n, block_k, K);
     if (pc && variant != BI8_GEMM_AUTO)
         return fail(BI8_ERR_SHAPE, "%s: the per-channel form has one kernel (variant must be AUTO)", fn);
-    if (variant == BI8_GEMM_SKINNY && M > 32)
-        return fail(BI8_ERR_SHAPE, "%s: the skinny kernel takes M <= 32, got %lld", fn, (long long)M);
+    if (variant == BI8_GEMM_SKINNY && M > 64)
+        return fail(BI8_ERR_SHAPE, "%s: the skinny kernel takes M <= 64, got %lld", fn, (long long)M);
     if (M == 0) return ok();
     if (bias && !aligned(bias, 2)) return fail(BI8_ERR_ALIGN, "%s: bias must be 2-byte aligned", fn);
     if (pc)

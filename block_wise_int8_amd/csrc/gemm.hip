@@ -16,12 +16,12 @@
 // t = xs[m, g] * ws[n / 128, g], applied as y = fma(float(acc_int32), t, y).
 //
 // Paths:
-//  * skinny (M <= 32, decode): HBM streaming of W.  A workgroup owns 16
-//    weight rows; its 8 waves split K.  Each lane loads 32 contiguous bytes of
+//  * skinny (decode; M <= 64 with N small enough): HBM streaming of W.  A
+//    workgroup owns 16 weight rows; its 8 waves split K.  Each lane loads 32 contiguous bytes of
 //    one weight row per 128-block straight into registers (no LDS), issues all
 //    of its loads before the first MFMA (v_mfma_i32_16x16x64_i8), and the
 //    waves' fp32 partials are summed through LDS.
-//  * tiled (M > 32, prefill, MoE): int8 MFMA v_mfma_i32_32x32x32_i8.  A
+//  * tiled (the other shapes: prefill, MoE): int8 MFMA v_mfma_i32_32x32x32_i8.  A
 //    workgroup computes a (64*WN) x (64*WM) tile (W rows x X rows), one 64x64
 //    sub-tile per wave.  K advances one 128-block per step; both operand tiles
 //    are staged in LDS by buffer->LDS loads (no VGPR round trip) through a
@@ -69,18 +69,27 @@ __device__ __forceinline__ i32x4 as_i32x4(u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny path (M <= 32)
+// Skinny path (M <= 64)
 // ---------------------------------------------------------------------------
 
 constexpr int kSkinnyWaves = 8;
+constexpr int64_t kSkinnyMaxM = 64;
+// Crossovers at K = 4096 (skinny / tiled, us): block form M = 24, N = 8192:
+// 17.4 / 18.6, M = 32, N = 8192: 19.6 / 18.8, M = 8, N = 28672: 31.0 / 27.0;
+// per-channel M = 16, N = 28672: 32.0 / 37.0, M = 24, N = 28672: 38.2 / 35.4.
+constexpr int64_t kSkinnyBudget = 360000;     // block form
+constexpr int64_t kSkinnyBudgetPC = 1024000;  // per-channel form
 constexpr int kSkinnyUnroll = 4;
 
-// MT: 16-token column tiles (1 for M <= 16, 2 for M <= 32).  PC: the
+// MT: 16-token column tiles (1 to 4: M <= 16, 32, 48, 64).  PC: the
 // per-channel form (blocks of 1 x K): the block sums are added unscaled and
 // the token and weight-row scales multiply once, in the store.
 template <int MT, bool PC>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs p,
                                                                        int32_t blocks_per_wave) {
+    // loads of U K blocks are in flight per wave (fewer with more token
+    // tiles: the activation operands take registers too)
+    constexpr int U = MT <= 2 ? kSkinnyUnroll : 2;
     __shared__ float red[kSkinnyWaves][MT][64][4];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -104,13 +113,13 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) yv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t b0 = b_begin; b0 < b_end; b0 += kSkinnyUnroll) {
-        i32x4 wa[kSkinnyUnroll][2];
-        i32x4 xb[kSkinnyUnroll][MT][2];
-        float xsv[kSkinnyUnroll][MT];
-        float wsv[kSkinnyUnroll];
+    for (int64_t b0 = b_begin; b0 < b_end; b0 += U) {
+        i32x4 wa[U][2];
+        i32x4 xb[U][MT][2];
+        float xsv[U][MT];
+        float wsv[U];
 #pragma unroll
-        for (int u = 0; u < kSkinnyUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t b = b0 + u;
             const bool ok = b < b_end;
             const int64_t kk = b * kBlock + quad * 32;
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
         // round trips instead of one
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kSkinnyUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], xb[u][mt][0],
@@ -1091,6 +1100,24 @@ template __global__ void gemm_wide_kernel<false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true>(GemmArgs);
 
+// One workgroup per 16 weight rows; 16-token tiles by M.
+template <bool PC>
+hipError_t launch_skinny(GemmArgs p, hipStream_t stream) {
+    const int64_t tiles = (p.N + 15) / 16;
+    if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
+    const dim3 grid((unsigned)tiles), block(kSkinnyWaves * 64);
+    if (p.M <= 16)
+        hipLaunchKernelGGL((gemm_skinny_kernel<1, PC>), grid, block, 0, stream, p, bpw);
+    else if (p.M <= 32)
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, PC>), grid, block, 0, stream, p, bpw);
+    else if (p.M <= 48)
+        hipLaunchKernelGGL((gemm_skinny_kernel<3, PC>), grid, block, 0, stream, p, bpw);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<4, PC>), grid, block, 0, stream, p, bpw);
+    return hipGetLastError();
+}
+
 template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS>
 hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
     using C = TileCfg<WN, WM, SA, SB>;
@@ -1138,9 +1165,21 @@ GemmArgs make_args(const int8_t *xq, const float *xs, const int8_t *w, const flo
 // once its tiles fill the 256 CUs (prefill, gate_up); with fewer (down) the
 // 256 x 128 kernel, with twice the tiles, is faster; 128 x 64 keeps small
 // problems spread over the chip.
+// The skinny kernel reads every activation row once per 16 weight rows, so
+// it moves N * K * (1 + M / 16) bytes from L2 and HBM, at a rate close to
+// the same for every shape; the tiled kernels read each byte far fewer times
+// but, with a grid of few tiles, run one workgroup per CU at a pace per K
+// block that does not depend on N.  Both times scale with K, so the choice
+// is a budget on N * (16 + M), measured on each form (the per-channel tiled
+// kernels have larger tiles, so fewer of them).
+static bool use_skinny(int64_t M, int64_t N, bool per_channel) {
+    if (M > kSkinnyMaxM) return false;
+    return N * (16 + M) <= (per_channel ? kSkinnyBudgetPC : kSkinnyBudget);
+}
+
 GemmPath select_gemm_path(int64_t M, int64_t N, int64_t K) {
     (void)K;
-    if (M <= 32) return GemmPath::kSkinny;
+    if (use_skinny(M, N, false)) return GemmPath::kSkinny;
     if (((M + 255) / 256) * ((N + 255) / 256) >= 256) return GemmPath::kTile256x256;
     if (((M + 127) / 128) * ((N + 255) / 256) >= 256) return GemmPath::kTile256x128;
     return GemmPath::kTile128x64;
@@ -1162,17 +1201,8 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
     if (path == GemmPath::kAuto) path = select_gemm_path(M, N, K);
     switch (path) {
         case GemmPath::kSkinny: {
-            if (M > 32) return hipErrorInvalidValue;
-            const int64_t tiles = (N + 15) / 16;
-            if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
-            const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
-            if (M <= 16)
-                hipLaunchKernelGGL((gemm_skinny_kernel<1, false>), dim3((unsigned)tiles),
-                                   dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
-            else
-                hipLaunchKernelGGL((gemm_skinny_kernel<2, false>), dim3((unsigned)tiles),
-                                   dim3(kSkinnyWaves * 64), 0, stream, p, bpw);
-            return hipGetLastError();
+            if (M > kSkinnyMaxM) return hipErrorInvalidValue;
+            return launch_skinny<false>(p, stream);
         }
         case GemmPath::kTile256x256:
             p.tiles_m = (M + 255) / 256;
@@ -1200,18 +1230,7 @@ hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8
                                    hipStream_t stream) {
     GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
     p.NB = N;   // one scale per weight row
-    if (M <= 32) {
-        const int64_t tiles = (N + 15) / 16;
-        if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
-        const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
-        if (M <= 16)
-            hipLaunchKernelGGL((gemm_skinny_kernel<1, true>), dim3((unsigned)tiles), dim3(kSkinnyWaves * 64), 0,
-                               stream, p, bpw);
-        else
-            hipLaunchKernelGGL((gemm_skinny_kernel<2, true>), dim3((unsigned)tiles), dim3(kSkinnyWaves * 64), 0,
-                               stream, p, bpw);
-        return hipGetLastError();
-    }
+    if (use_skinny(M, N, true)) return launch_skinny<true>(p, stream);
     if (((M + 255) / 256) * ((N + 255) / 256) >= 256) {
         // enough 256 x 256 tiles to fill the chip
         p.tiles_m = (M + 255) / 256;

@@ -297,13 +297,13 @@ int32_t blockint8_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_
  * shape; the *_variant entry points run a named one instead, with the same
  * arguments, results and errors, so that every kernel can be checked and
  * timed on any shape it accepts.  A variant that cannot run the shape
- * (BI8_GEMM_SKINNY with more than 32 rows, BI8_GEMM_SKINNY or
+ * (BI8_GEMM_SKINNY with more than 64 rows, BI8_GEMM_SKINNY or
  * BI8_GEMM_TILE_128X64 for the grouped GEMM) returns BI8_ERR_SHAPE; an
  * unknown variant id returns BI8_ERR_SHAPE.  The per-channel form ([1, K]
  * blocks) has a single kernel: only BI8_GEMM_AUTO runs it.
  *
  *   BI8_GEMM_AUTO          the shape-based choice
- *   BI8_GEMM_SKINNY        M <= 32: weight rows streamed into registers
+ *   BI8_GEMM_SKINNY        M <= 64: weight rows streamed into registers
  *   BI8_GEMM_TILE_128X64   128 weight rows x 64 activation rows per workgroup
  *   BI8_GEMM_TILE_256X128  256 x 128
  *   BI8_GEMM_TILE_256X256  256 x 256

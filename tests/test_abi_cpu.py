@@ -154,7 +154,12 @@ def test_variant_ids_match_header():
 
 @pytest.mark.parametrize("M,N,K,variant", [
     (1, 4096, 4096, bi8.GEMM_SKINNY), (32, 100, 128, bi8.GEMM_SKINNY),
-    (33, 4096, 4096, bi8.GEMM_TILE_128X64), (333, 5000, 4000, bi8.GEMM_TILE_128X64),
+    (33, 4096, 4096, bi8.GEMM_SKINNY), (64, 4096, 4096, bi8.GEMM_SKINNY),
+    # the skinny kernel's traffic grows with N * (16 + M): past a budget the
+    # tiled kernel runs, also for few tokens
+    (64, 8192, 4096, bi8.GEMM_TILE_128X64), (32, 8192, 4096, bi8.GEMM_TILE_128X64),
+    (8, 28672, 4096, bi8.GEMM_TILE_128X64), (65, 100, 128, bi8.GEMM_TILE_128X64),
+    (333, 5000, 4000, bi8.GEMM_TILE_128X64),
     (2048, 4096, 14336, bi8.GEMM_TILE_256X128), (4096, 4096, 4096, bi8.GEMM_TILE_256X256),
     (2048, 28672, 4096, bi8.GEMM_TILE_256X256), (8192, 8192, 1024, bi8.GEMM_TILE_256X256),
 ])
@@ -178,7 +183,7 @@ def gemm_v(lib, variant, M=4, xq=P16, **kw):
 
 @pytest.mark.parametrize("variant,M,kw,status", [
     (-1, 4, {}, SHAPE), (5, 4, {}, SHAPE), (99, 4, {}, SHAPE),
-    (bi8.GEMM_SKINNY, 33, {}, SHAPE),                       # skinny takes M <= 32
+    (bi8.GEMM_SKINNY, 65, {}, SHAPE),                       # skinny takes M <= 64
     (bi8.GEMM_TILE_256X256, 64, dict(xq=None), NULL),
     (bi8.GEMM_TILE_256X128, 64, dict(bk=64), BLOCK),
     (bi8.GEMM_TILE_128X64, 64, dict(K=72), ALIGN),

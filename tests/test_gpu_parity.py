@@ -150,12 +150,14 @@ TILED = [bi8.GEMM_TILE_128X64, bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]
 
 
 SHAPES = [
-    # skinny path (M <= 32)
+    # skinny path
     (1, 16, 16), (1, 256, 256), (8, 4096, 512), (8, 100, 4000), (16, 300, 144), (17, 257, 1040),
     (32, 512, 384), (5, 1000, 4096), (32, 100, 2000), (31, 64, 2096), (3, 40, 21840),
-    # tiled small and large paths, ragged N / K / M
+    # more tokens (tiled, or skinny while N is small), ragged N / K / M
     (33, 256, 256), (64, 128, 128), (100, 1000, 272), (129, 384, 400), (333, 500, 4000),
     (256, 2048, 256), (300, 5000, 128), (200, 7, 128), (1000, 16, 64), (513, 1024, 1024),
+    # skinny with 3 and 4 token tiles; few tokens on a wide N (tiled by choice)
+    (40, 1000, 1040), (64, 520, 2064), (48, 300, 4000), (8, 28672, 256),
 ]
 
 
@@ -166,7 +168,7 @@ def test_gemm_shapes_vs_oracle(M, N, K):
     y_ref = oracle.gemm(xq, xs, w, ws)
     y = run_gemm(xq, xs, w, ws)
     assert_gemm_close(y, y_ref, "M=%d N=%d K=%d" % (M, N, K))
-    variants = TILED + ([bi8.GEMM_SKINNY] if M <= 32 else [])
+    variants = TILED + ([bi8.GEMM_SKINNY] if M <= 64 else [])
     for v in variants:
         assert_gemm_close(run_gemm(xq, xs, w, ws, variant=v), y_ref, "M=%d N=%d K=%d variant %d" % (M, N, K, v))
 

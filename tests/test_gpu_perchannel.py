@@ -36,7 +36,8 @@ def pc_case(seed, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (8, 4096, 4096), (200, 1000, 1040), (513, 520, 4000),
-                                   (4096, 4096, 4096), (33, 7, 16), (4000, 4100, 1040)])
+                                   (4096, 4096, 4096), (33, 7, 16), (4000, 4100, 1040),
+                                   (40, 1000, 1040), (64, 520, 2064), (24, 28672, 256)])
 def test_per_channel_gemm_vs_oracle(M, N, K):
     x, w, ws = pc_case((M, N, K, 1), M, N, K)
     xq, xs = oracle.quant_act(x, block_k=K)
