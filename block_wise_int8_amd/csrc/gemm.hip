@@ -87,9 +87,9 @@ constexpr int kSkinnyUnroll = 4;
 template <int MT, bool PC>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs p,
                                                                        int32_t blocks_per_wave) {
-    // loads of U K blocks are in flight per wave (fewer with more token
-    // tiles: the activation operands take registers too)
-    constexpr int U = MT <= 2 ? kSkinnyUnroll : 2;
+    // loads of U K blocks are in flight per wave (fewer with 4 token tiles:
+    // the activation operands take registers too)
+    constexpr int U = MT <= 3 ? kSkinnyUnroll : 2;
     __shared__ float red[kSkinnyWaves][MT][64][4];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
