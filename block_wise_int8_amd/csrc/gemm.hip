@@ -1095,7 +1095,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_perch_wide_kernel(Gemm
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true, 3>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true, 3>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 4>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4>(GemmArgs);
 template __global__ void gemm_wide_kernel<false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true>(GemmArgs);
@@ -1216,9 +1216,11 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
             p.tiles_m = (M + 63) / 64;
             p.tiles_n = (N + 127) / 128;
             // A grid that leaves CUs idle runs one workgroup per CU: a fourth
-            // stage (96 KB of LDS) lets the loads run a block further ahead.
+            // stage (96 KB of LDS) lets the loads run a block further ahead,
+            // and the waves run in step (no ping-pong: with one workgroup
+            // per CU its second barrier per block costs more than it hides).
             // A larger grid keeps the 72 KB ring, two workgroups per CU.
-            if (p.tiles_m * p.tiles_n <= 256) return launch_tiled<4, 2, 1, 1, false, true, 4>(p, stream);
+            if (p.tiles_m * p.tiles_n <= 256) return launch_tiled<4, 2, 1, 1, false, false, 4>(p, stream);
             return launch_tiled<4, 2, 1, 1, false, true, 3>(p, stream);
         default:
             return hipErrorInvalidValue;
