@@ -4,10 +4,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the hot path over one batch of synthetic input already
-resident in HBM: dynamic activation quantisation (bf16 -> int8 + fp32 scales)
-followed by the block-scaled int8 GEMM (the grouped GEMM for ``moe``: both
-w13 and w2 projections, each with its quantisation pass).  The default
-workload is the decode-shaped linear, M=8 tokens, K=N=4096, [128,128] blocks.
+resident in HBM.  The default workload is the block-INT8 FusedMoE layer, the
+largest of the measured configurations (4096 tokens, hidden 4096,
+intermediate 14336, top-2 of 8 experts, [128,128] blocks): route, gather +
+quantise, w13 grouped GEMM, SiLU gating + requantise, w2 grouped GEMM,
+combine.  The dense workloads (``--workload decode|prefill|...``) step
+through dynamic activation quantisation (bf16 -> int8 + fp32 scales)
+followed by the block-scaled int8 GEMM.
 
 Weights rotate over enough distinct copies (>= 540 MB in total) that the
 256 MB Infinity Cache cannot hold them, so HBM is what is measured.  K steps
@@ -16,17 +19,22 @@ bracketed by synchronisation.
 
 Prints ONE JSON line (rank 0, N=1) with the throughput, a ``roofline`` object
 for the dominant kernel (its average launch time measured with HIP events on
-its stream) and a ``cpu_baseline`` object (the CPU oracle timed on a bounded
-sample of the same workload, on this host).
+its stream, and the average GFX clock over that timed region read from the
+shader-clock counters), the same for the decode and prefill GEMMs under
+``roofline_other`` (with the MoE default), and a ``cpu_baseline`` object (the
+CPU oracle timed on a bounded sample of the same workload on this host, on
+one core and on all the cores this process may use).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -43,6 +51,7 @@ VARIANTS = {"auto": None, "skinny": bi8.GEMM_SKINNY, "128x64": bi8.GEMM_TILE_128
             "256x128": bi8.GEMM_TILE_256X128, "256x256": bi8.GEMM_TILE_256X256}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items() if v is not None}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
+PEAK_CLOCK_MHZ = 2400.0        # the GFX clock the published int8 peak assumes (256 CUs)
 ROTATE_BYTES = 540 << 20       # > Infinity Cache (256 MB)
 MAX_COPIES = 64
 
@@ -127,24 +136,41 @@ class Dense:
                 "block": list(self.block), "weight_copies": self.copies,
                 "kernel": "per-channel" if self.per_channel else VARIANT_NAMES[v]}
 
-    def cpu_sample(self, budget_s):
-        """Time the oracle (quant + GEMM) on a bounded sample of rows."""
+    def cpu_sample(self, budget_s, threads=1):
+        """Time the oracle (quant + GEMM) on a bounded sample of token rows.
+        With threads > 1 the unchanged single-threaded oracle GEMM runs on
+        disjoint slices of the weight rows (whole scale blocks), one per
+        thread (the oracle's C code runs with the GIL released)."""
         import oracle
-        # one row costs N*K MACs; pick rows to fill roughly the budget
-        t0 = time.perf_counter()
-        xq, xs = oracle.quant_act(self.x_np[:1], block_k=self.block[1])
-        oracle.gemm(xq, xs, self.w_np, self.ws_np, block=self.block)
-        t_row = max(time.perf_counter() - t0, 1e-4)
-        rows = int(max(1, min(self.M, budget_s / t_row)))
-        reps = int(max(1, min(1000, budget_s / (t_row * rows))))
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            xq, xs = oracle.quant_act(self.x_np[:rows], block_k=self.block[1])
-            oracle.gemm(xq, xs, self.w_np, self.ws_np, block=self.block)
-        dt = time.perf_counter() - t0
+        bn = self.block[0]
+        nblk = -(-self.N // bn)
+        n_sl = max(1, min(threads, nblk))
+        edges = [min(self.N, bn * (nblk * i // n_sl)) for i in range(n_sl + 1)]
+        slices = [(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+        oracle.scale_shape(1, 1)   # load the library before any thread does
+
+        def gemm_slice(args):
+            xq, xs, (a, b) = args
+            return oracle.gemm(xq, xs, self.w_np[a:b], self.ws_np[a // bn:-(-b // bn)], block=self.block)
+
+        with ThreadPoolExecutor(len(slices)) as ex:
+            def once(rows):
+                xq, xs = oracle.quant_act(self.x_np[:rows], block_k=self.block[1])
+                list(ex.map(gemm_slice, [(xq, xs, sl) for sl in slices]))
+
+            t0 = time.perf_counter()
+            once(1)   # one row costs N*K MACs: size the sample from it
+            t_row = max(time.perf_counter() - t0, 1e-4)
+            rows = int(max(1, min(self.M, budget_s / t_row)))
+            reps = int(max(1, min(1000, budget_s / (t_row * rows))))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                once(rows)
+            dt = time.perf_counter() - t0
         ops = 2.0 * rows * self.N * self.K * reps
-        return ops / dt / 1e12, "%d of %d token rows x all N, quant+GEMM, %d repetition(s), %.1f s" % (
-            rows, self.M, reps, dt)
+        return ops / dt / 1e12, len(slices), (
+            "%d of %d token rows x all N, quant+GEMM, %d repetition(s), %.1f s%s" %
+            (rows, self.M, reps, dt, ", N split over %d threads" % len(slices) if len(slices) > 1 else ""))
 
 
 class Moe:
@@ -237,31 +263,41 @@ class Moe:
                 "hidden": self.H, "intermediate": self.I, "rows": self.R, "block": [128, 128],
                 "kernel": VARIANT_NAMES[v]}
 
-    def cpu_sample(self, budget_s):
+    def cpu_sample(self, budget_s, threads=1):
         """Time the oracle's layer (route, quantise, w13 GEMM, SiLU, requantise,
-        w2 GEMM, combine) on a bounded sample of tokens."""
+        w2 GEMM, combine) on a bounded sample of tokens.  With threads > 1 the
+        unchanged single-threaded oracle runs the layer on disjoint token
+        slices, one per thread (each token's result depends on its own row
+        only; the oracle's C code runs with the GIL released)."""
         import oracle
         ids, wts = oracle.topk_softmax(self.logits_np, self.k)
 
         def layer(tokens):
-            n = len(tokens)
             st, off, row_of = oracle.moe_align(ids[tokens], self.E)
             xq, xs = oracle.quant_act(self.x_np[tokens][st])
             h = oracle.moe_gemm(xq, xs, off, self.w13_np, self.ws13_np)
             aq, as_ = oracle.quant_act(oracle.silu_mul(h))
             y2 = oracle.moe_gemm(aq, as_, off, self.w2_np, self.ws2_np)
             oracle.combine(y2, row_of, wts[tokens].astype(np.float32))
-            return n
+            return len(tokens)
 
-        t0 = time.perf_counter()
-        layer(np.arange(1))
-        t_tok = max(time.perf_counter() - t0, 1e-4)
-        n = int(max(1, min(self.T, budget_s / t_tok)))
-        t0 = time.perf_counter()
-        layer(np.arange(n))
-        dt = time.perf_counter() - t0
-        ops = 2.0 * n * self.k * (2 * self.I * self.H + self.H * self.I)
-        return ops / dt / 1e12, "first %d of %d tokens through the whole layer, %.1f s" % (n, self.T, dt)
+        threads = max(1, min(threads, self.T))
+        with ThreadPoolExecutor(threads) as ex:
+            def run(n):
+                edges = np.linspace(0, n, threads + 1).astype(int)
+                return sum(ex.map(layer, [np.arange(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]))
+
+            t0 = time.perf_counter()
+            run(threads)   # one token per thread: size the sample from it
+            t_round = max(time.perf_counter() - t0, 1e-4)
+            n = int(max(threads, min(self.T, threads * budget_s / t_round)))
+            t0 = time.perf_counter()
+            done = run(n)
+            dt = time.perf_counter() - t0
+        ops = 2.0 * done * self.k * (2 * self.I * self.H + self.H * self.I)
+        return ops / dt / 1e12, threads, (
+            "first %d of %d tokens through the whole layer, %.1f s%s" %
+            (done, self.T, dt, ", token slices over %d threads" % threads if threads > 1 else ""))
 
 
 def make_workload(name, copies=None, variant=None, per_channel=False):
@@ -278,13 +314,64 @@ def capture(fn, steps):
     return g
 
 
-def timed(fn, steps, use_graph):
-    """Run ``steps`` calls of fn; return (wall seconds, event seconds)."""
+class ClockProbe:
+    """Average GFX clock over a timed region, from the shader-clock counters.
+
+    ``libbi8clock.so`` launches a few one-wave workgroups that record the
+    shader-clock cycle counter, the constant-rate real-time counter and the
+    XCD they ran on.  One launch before and one after the region, on the same
+    stream, give per XCD: cycles / real time = the average clock over the
+    region (the launches bracket it, so the figure includes the few
+    microseconds of launch gaps at its ends)."""
+
+    BLOCKS = 64   # dispatched round-robin over the XCDs: several per XCD
+
+    def __init__(self):
+        path = os.path.join(ROOT, "block_wise_int8_amd", "libbi8clock.so")
+        self.lib = ctypes.CDLL(path)
+        self.lib.bi8clock_sample.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        self.lib.bi8clock_sample.restype = ctypes.c_int
+        self.lib.bi8clock_wall_rate_khz.argtypes = [ctypes.c_int]
+        self.lib.bi8clock_wall_rate_khz.restype = ctypes.c_int
+        self.rate_khz = self.lib.bi8clock_wall_rate_khz(torch.cuda.current_device())
+        self.buf = torch.zeros((2, self.BLOCKS, 3), dtype=torch.int64, device="cuda")
+
+    def mark(self, i, stream):
+        rc = self.lib.bi8clock_sample(ctypes.c_void_p(self.buf[i].data_ptr()), self.BLOCKS,
+                                      ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("clock probe launch failed (%d)" % rc)
+
+    def read(self):
+        """{"mhz": mean over XCDs, "min", "max", "xcds"} after both marks, or None."""
+        if self.rate_khz <= 0:
+            return None
+        b = self.buf.cpu().numpy()
+        per_xcd = []
+        for x in sorted(set(b[0, :, 2].tolist()) & set(b[1, :, 2].tolist())):
+            i0 = np.nonzero(b[0, :, 2] == x)[0][0]
+            i1 = np.nonzero(b[1, :, 2] == x)[0][0]
+            dt, dr = b[1, i1, 0] - b[0, i0, 0], b[1, i1, 1] - b[0, i0, 1]
+            if dt > 0 and dr > 0:
+                per_xcd.append(dt / dr * self.rate_khz / 1e3)
+        if not per_xcd:
+            return None
+        f = np.array(per_xcd)
+        if not (100.0 <= f.mean() <= 4000.0):   # not a shader clock: do not report it
+            return None
+        return {"mhz": round(float(f.mean()), 1), "min": round(float(f.min()), 1),
+                "max": round(float(f.max()), 1), "xcds": len(f)}
+
+
+def timed(fn, steps, use_graph, clock=None):
+    """Run ``steps`` calls of fn; return (wall seconds, event seconds, clock)."""
     g = capture(fn, steps) if use_graph else None
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if clock is not None:
+        clock.mark(0, stream)
     e0.record(stream)
     if g is not None:
         g.replay()
@@ -292,9 +379,35 @@ def timed(fn, steps, use_graph):
         for i in range(steps):
             fn(i)
     e1.record(stream)
+    if clock is not None:
+        clock.mark(1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, e0.elapsed_time(e1) / 1e3
+    return wall, e0.elapsed_time(e1) / 1e3, (clock.read() if clock is not None else None)
+
+
+def roofline(w, t_dom, clk):
+    """The dominant kernel's roofline object: achieved / published peak, and
+    the int8 peak scaled to the clock observed while it ran."""
+    hbm_bound = w.dominant_ops / (INT8_PEAK_TOPS * 1e12) < w.dominant_bytes / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        achieved = w.dominant_bytes / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = w.dominant_ops / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    roof["kernel"] = w.dominant
+    roof["avg_launch_us"] = round(t_dom * 1e6, 3)
+    roof["algorithmic_bytes"] = w.dominant_bytes
+    roof["algorithmic_ops"] = w.dominant_ops
+    roof["clock_mhz"] = clk
+    if clk is not None and not hbm_bound:
+        peak_clk = INT8_PEAK_TOPS * clk["mhz"] / PEAK_CLOCK_MHZ
+        roof["peak_at_clock"] = round(peak_clk, 1)
+        roof["frac_at_clock"] = round(achieved / peak_clk, 4)
+    return roof
 
 
 def source_digest():
@@ -325,9 +438,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(wl.CONFIGS))
+    ap.add_argument("--workload", default="moe", choices=sorted(wl.CONFIGS))
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for each cpu_baseline leg (one core, all cores)")
+    ap.add_argument("--other", default="decode,prefill",
+                    help="with the moe workload, also time the dominant GEMM of these dense workloads "
+                         "(comma-separated; empty for none) under roofline_other")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS),
                     help="GEMM kernel (default: the library's shape-based choice)")
@@ -366,6 +483,7 @@ def main():
         sys.exit(2)
     w = make_workload(args.workload, args.copies, VARIANTS[args.variant], args.per_channel)
     use_graph = not args.eager
+    clock = ClockProbe()
 
     log("[bench] warmup %d steps" % args.warmup)
     for i in range(args.warmup):
@@ -373,45 +491,52 @@ def main():
     torch.cuda.synchronize()
 
     log("[bench] timing %d steps (%s)" % (args.steps, "graph" if use_graph else "eager"))
-    wall, ev = timed(w.step, args.steps, use_graph)
+    wall, ev, clk_step = timed(w.step, args.steps, use_graph, clock)
     ms_per_step = wall / args.steps * 1e3
 
     log("[bench] timing the dominant kernel (%s) alone" % w.dominant)
-    _, ev_dom = timed(w.dominant_launch, args.steps, use_graph)
+    _, ev_dom, clk_dom = timed(w.dominant_launch, args.steps, use_graph, clock)
     t_dom = ev_dom / args.steps
-    _, ev_q = timed(w.quant, args.steps, use_graph)
+    _, ev_q, _ = timed(w.quant, args.steps, use_graph)
     t_q = ev_q / args.steps
 
     parts = None
     if hasattr(w, "parts"):
         parts = {}
         for name, (fn, nbytes) in w.parts().items():
-            _, ev_p = timed(fn, args.steps, use_graph)
+            _, ev_p, _ = timed(fn, args.steps, use_graph)
             t_p = ev_p / args.steps
             parts[name] = {"avg_launch_us": round(t_p * 1e6, 3), "GB/s": round(nbytes / t_p / 1e9, 1)}
     value = w.ops / (wall / args.steps) / 1e12
-    hbm_bound = w.dominant_ops / (INT8_PEAK_TOPS * 1e12) < w.dominant_bytes / (HBM_PEAK_GBS * 1e9)
-    if hbm_bound:
-        achieved = w.dominant_bytes / t_dom / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = w.dominant_ops / t_dom / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    roof["kernel"] = w.dominant
-    roof["avg_launch_us"] = round(t_dom * 1e6, 3)
-    roof["algorithmic_bytes"] = w.dominant_bytes
-    roof["algorithmic_ops"] = w.dominant_ops
+    roof = roofline(w, t_dom, clk_dom)
     # the counters were taken with the default kernel choice of the block form
     roof["traffic"] = (counter_traffic(args.workload)
                        if args.variant == "auto" and not args.per_channel else None)
+
+    others = None
+    if args.workload == "moe" and args.other:
+        others = {}
+        for name in [n for n in args.other.split(",") if n]:
+            log("[bench] timing the dominant kernel of %s alone" % name)
+            o = make_workload(name)
+            for i in range(min(args.warmup, 10)):
+                o.step(i)
+            o.quant(0)
+            _, ev_o, clk_o = timed(o.dominant_launch, args.steps, use_graph, clock)
+            r = roofline(o, ev_o / args.steps, clk_o)
+            r["traffic"] = counter_traffic(name)
+            r["config"] = o.config()
+            others[name] = r
+            del o
+        torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic", "config": w.config(), "roofline": roof,
+        "roofline_other": others,
+        "clock_mhz_step": clk_step,
         "quant_act": {"avg_launch_us": round(t_q * 1e6, 3),
                       "GB/s": round(quant_bytes(*w.quant_shape) / t_q / 1e9, 1)},
         "steps_alone": parts,
@@ -419,13 +544,28 @@ def main():
         "timing": "hip graph of %d steps, one replay" % args.steps if use_graph else "eager launches",
     }
     if not args.no_cpu:
-        log("[bench] cpu baseline (oracle, ~%.0f s)" % args.cpu_budget)
-        cpu_tops, sample = w.cpu_sample(args.cpu_budget)
-        out["cpu_baseline"] = {"value": round(cpu_tops, 6), "unit": "TOPS", "cores": 1,
-                               "kind": "oracle", "sample": sample}
+        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        log("[bench] cpu baseline (oracle, one core, ~%.0f s)" % args.cpu_budget)
+        v1, _, s1 = w.cpu_sample(args.cpu_budget, 1)
+        log("[bench] cpu baseline (oracle, %d threads, ~%.0f s)" % (cores, args.cpu_budget))
+        vn, used, sn = w.cpu_sample(args.cpu_budget, cores)
+        out["cpu_baseline"] = {"value": round(vn, 6), "unit": "TOPS", "cores": used, "kind": "oracle",
+                               "sample": sn, "cpu_model": cpu_model(),
+                               "one_core": {"value": round(v1, 6), "cores": 1, "sample": s1}}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -21,8 +21,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libblockint8.so")
+# the benchmark's shader-clock probe, a library of its own (not the product path)
+CLOCK_LIB_PATH = os.path.join(PKG, "libbi8clock.so")
 
 SOURCES = ["abi.cpp", "quant_act.hip", "gemm.hip", "moe.hip"]
+CLOCK_SOURCES = ["clockprobe.hip"]
 ARCH = "gfx950"
 
 
@@ -43,13 +46,13 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+def _build_lib(sources: list[str], lib_path: str, verbose: bool, extra_flags: list[str] | None) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     flags = compile_flags() + list(extra_flags or [])
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
@@ -69,14 +72,20 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    tmp = lib_path + ".tmp%d" % os.getpid()
     link = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
     check_symbols(tmp)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Build libblockint8.so (and the benchmark's clock probe library)."""
+    _build_lib(CLOCK_SOURCES, CLOCK_LIB_PATH, verbose, extra_flags)
+    return _build_lib(SOURCES, LIB_PATH, verbose, extra_flags)
 
 
 def check_symbols(path: str) -> None:

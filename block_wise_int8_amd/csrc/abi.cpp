@@ -255,6 +255,11 @@ int32_t blockint8_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t 
     return hip_status(fn, bi8::launch_quant_weight(w, N, K, ldw, wq, ws, static_cast<hipStream_t>(stream)));
 }
 
+// Section 3 of the page: a block-quantised weight may be cut between
+// tensor-parallel ranks only where a cut cannot split a scale block.  Every
+// shard edge along a split axis is walked and tested against the block edge
+// of that axis: block_k columns on the input axis, block_n rows on the
+// output axis.
 int32_t blockint8_check_tp_partition(int64_t input_size, int64_t input_size_per_partition,
                                      const int64_t *output_partition_sizes, int32_t n_out,
                                      int32_t tp_size, int32_t block_n, int32_t block_k) {
@@ -263,17 +268,36 @@ int32_t blockint8_check_tp_partition(int64_t input_size, int64_t input_size_per_
         n_out < 0)
         return fail(BI8_ERR_SHAPE, "%s: sizes, tp_size and block dimensions must be positive", fn);
     if (n_out > 0 && !output_partition_sizes) return fail(BI8_ERR_NULL, "%s: NULL output_partition_sizes", fn);
-    if (tp_size > 1 && input_size / input_size_per_partition == tp_size &&
-        input_size_per_partition % block_k != 0)
-        return fail(BI8_ERR_BLOCK, "%s: input size per partition %lld is not a multiple of block_k = %d",
-                    fn, (long long)input_size_per_partition, block_k);
+
+    // Input axis: the row-parallel layout hands each of the tp_size ranks a
+    // run of input_size_per_partition columns (the ranks' runs make up the
+    // input, up to the rounding of the division); rank r's run starts at
+    // column r * input_size_per_partition.  In any other layout the input
+    // axis is not cut.
+    const bool input_axis_cut = tp_size > 1 && input_size / input_size_per_partition == tp_size;
+    for (int32_t r = 1; input_axis_cut && r < tp_size; ++r) {
+        const int64_t first_col = (int64_t)r * input_size_per_partition;
+        if (first_col % block_k != 0)
+            return fail(BI8_ERR_BLOCK,
+                        "%s: rank %d's input columns start at %lld, inside a scale block of %d columns "
+                        "(input_size_per_partition = %lld)",
+                        fn, r, (long long)first_col, block_k, (long long)input_size_per_partition);
+    }
+
+    // Output axis: the output partitions sit end to end along the weight's
+    // rows (e.g. the fused gate and up projections); the row after each one
+    // must start a scale block.
+    int64_t next_row = 0;
     for (int32_t i = 0; i < n_out; ++i) {
-        if (output_partition_sizes[i] <= 0)
-            return fail(BI8_ERR_SHAPE, "%s: output partition %d has size %lld", fn, i,
-                        (long long)output_partition_sizes[i]);
-        if (output_partition_sizes[i] % block_n != 0)
-            return fail(BI8_ERR_BLOCK, "%s: output partition size %lld is not a multiple of block_n = %d", fn,
-                        (long long)output_partition_sizes[i], block_n);
+        const int64_t rows = output_partition_sizes[i];
+        if (rows <= 0)
+            return fail(BI8_ERR_SHAPE, "%s: output partition %d has %lld rows", fn, i, (long long)rows);
+        next_row += rows;
+        if (next_row % block_n != 0)
+            return fail(BI8_ERR_BLOCK,
+                        "%s: output partition %d (%lld rows) ends inside a scale block of %d rows "
+                        "(its last row is %lld)",
+                        fn, i, (long long)rows, block_n, (long long)(next_row - 1));
     }
     return ok();
 }

@@ -190,13 +190,16 @@ int32_t blockint8_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t 
                                int32_t block_k, int8_t *wq, float *ws, void *stream);
 
 /*
- * Tensor-parallel partition check (section 3 of the page): block
- * quantisation needs the partition boundaries on block boundaries.
- *   row parallel:    when tp_size > 1 and input_size / input_size_per_partition
- *                    == tp_size, input_size_per_partition % block_k == 0;
- *   column parallel: every output_partition_sizes[i] % block_n == 0.
+ * Tensor-parallel partition check (section 3 of the page): with block
+ * quantisation, a cut between ranks must not split a scale block.
+ *   input axis:  when tp_size > 1 ranks each take input_size_per_partition
+ *                columns (input_size / input_size_per_partition == tp_size,
+ *                integer division), the first column of every rank after the
+ *                first must be a multiple of block_k;
+ *   output axis: the output partitions lie end to end along the rows, and
+ *                each must end on a multiple of block_n rows.
  * Host only (no device pointer, no launch).  Returns BI8_OK, or
- * BI8_ERR_BLOCK with the offending size in blockint8_last_error();
+ * BI8_ERR_BLOCK with the offending shard edge in blockint8_last_error();
  * BI8_ERR_NULL / BI8_ERR_SHAPE for a NULL array with n_out > 0 or a
  * non-positive size.
  */

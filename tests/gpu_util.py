@@ -3,8 +3,13 @@
 Holds none of the method's arithmetic: expected values always come from the
 oracle (or a library routine in a pin), never from here.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
+
+import oracle
 
 # Tolerance for the GEMM outputs: max |y_gpu - y_ref| / max |y_ref| per output
 # tensor.  The fp32 kernels and the fp64 oracle see identical int8 inputs and
@@ -57,3 +62,22 @@ def assert_gemm_close(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = ""):
     # rounding, so almost every element is within 1 bf16 ulp.
     assert frac_gt1 <= 0.01, "%s: %.3f%% of outputs more than 1 ulp apart" % (what, 100 * frac_gt1)
     return rel, frac_gt1, maxulp
+
+
+def host_threads() -> int:
+    """CPU threads this process may use (at most 16: the GPU machine's share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_gemm_rows(xq, xs, w, ws, bias=None):
+    """oracle.gemm on the given activation rows, split into row slices run on
+    a thread pool (the oracle call itself is unchanged and single-threaded;
+    each slice is an independent call on disjoint rows)."""
+    oracle.scale_shape(1, 1)   # load the library once, before the threads
+    M = xq.shape[0]
+    n = min(host_threads(), max(1, M))
+    bounds = np.linspace(0, M, n + 1).astype(int)
+    parts = [(a, b) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    with ThreadPoolExecutor(len(parts)) as ex:
+        outs = list(ex.map(lambda ab: oracle.gemm(xq[ab[0]:ab[1]], xs[ab[0]:ab[1]], w, ws, bias=bias), parts))
+    return np.concatenate(outs) if outs else np.zeros((0, w.shape[0]), np.uint16)

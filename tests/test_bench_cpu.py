@@ -84,3 +84,40 @@ def test_weight_copies_cover_the_cache():
     n = bench.n_copies(4096 * 4096)
     assert n * 4096 * 4096 >= 256 * 2**20
     assert bench.n_copies(4096 * 4096, override=3) == 3
+
+
+class _FakeBuf:
+    def __init__(self, a):
+        self.a = a
+
+    def cpu(self):
+        return self
+
+    def numpy(self):
+        return self.a
+
+
+def test_clock_probe_reads_cycles_over_real_time_per_xcd():
+    """Two samples per XCD: cycles / real-time ticks * tick rate = clock."""
+    import numpy as np
+    p = bench.ClockProbe.__new__(bench.ClockProbe)
+    p.rate_khz = 100000   # 100 MHz real-time counter
+    b = np.zeros((2, 4, 3), np.int64)
+    # XCD 0 at 2000 MHz (20 cycles per tick), XCD 1 at 2200 MHz; the second
+    # sample lists the XCDs in another order, as a later launch may
+    b[0] = [[1000, 500, 0], [7000, 501, 1], [1010, 502, 0], [7005, 503, 1]]
+    b[1] = [[7000 + 22 * 1000, 1501, 1], [1000 + 20 * 1000, 1500, 0], [0, 0, 1], [0, 0, 0]]
+    p.buf = _FakeBuf(b)
+    r = p.read()
+    assert r["xcds"] == 2 and r["min"] == 2000.0 and r["max"] == 2200.0 and r["mhz"] == 2100.0
+    p.rate_khz = 0
+    assert p.read() is None
+
+
+def test_roofline_scales_the_int8_peak_to_the_observed_clock():
+    class W:
+        dominant, dominant_ops, dominant_bytes = "k", 2 * 4096 ** 3, 67_600_000
+    r = bench.roofline(W, 100e-6, {"mhz": 1800.0, "min": 1790.0, "max": 1810.0, "xcds": 8})
+    assert r["bound"] == "mfma"
+    assert abs(r["achieved"] - 1374.4) < 0.1 and r["peak"] == 5000.0
+    assert r["peak_at_clock"] == 3750.0 and abs(r["frac_at_clock"] - 1374.4 / 3750.0) < 1e-4

@@ -161,3 +161,166 @@ def test_moe_layer_end_to_end(T, H, I, E, k, variant):
     rel, frac_gt1, _ = gemm_report(out, ref)
     assert rel <= GEMM_REL_TOL, "moe layer: max rel err %.3e" % rel
     assert frac_gt1 <= 0.05, "moe layer: %.3f%% of outputs more than 1 ulp apart" % (100 * frac_gt1)
+
+
+# ------------------------------------------------ the full-size MoE layer --
+#
+# The MoE workload at its real size (4096 tokens, hidden 4096, intermediate
+# 14336, top-2 of 8 experts), drawn exactly as the benchmark draws it, run
+# step by step on the GPU with every intermediate kept.  Every stage is
+# compared with the oracle on rows sampled in every 128-row tile of every
+# expert segment (so in every tile of each grouped-GEMM kernel, whose tiles
+# start at the segment starts), each fed the GPU's previous stage; and the
+# layer end to end on 64 tokens covering every expert, against the oracle's
+# pipeline computed from the inputs alone.
+
+MOE_VARIANTS = [None, bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]
+
+
+@pytest.fixture(scope="module")
+def moe_full():
+    c = wl.CONFIGS["moe"]
+    T, H, I, E, k = c["T"], c["H"], c["I"], c["E"], c["topk"]
+    rng = wl.rng_for(c["seed"])
+    x = wl.activations(rng, T, H)
+    logits = wl.router_logits(rng, T, E)
+    w13 = wl.weights(rng, E, 2 * I, H)
+    ws13 = wl.weight_scales(rng, E, *oracle.scale_shape(2 * I, H))
+    w2 = wl.weights(rng, E, H, I)
+    ws2 = wl.weight_scales(rng, E, *oracle.scale_shape(H, I))
+    d = dict(x=bf16_to_dev(x), logits=to_dev(logits), w13=to_dev(w13), ws13=to_dev(ws13), w2=to_dev(w2),
+             ws2=to_dev(ws2))
+    ids, wts, st, off, row_of = bi8.moe_route(d["logits"], k)
+    xq1, xs1 = bi8.quant_act_gather(d["x"], st)
+    h = bi8.moe_gemm(xq1, xs1, off, d["w13"], d["ws13"])
+    aq, as_, a = bi8.silu_mul_quant(h, return_a=True)
+    y2 = bi8.moe_gemm(aq, as_, off, d["w2"], d["ws2"])
+    out = bi8.moe_combine(y2, row_of, wts)
+    out_layer = bi8.moe_layer(d["x"], d["logits"], d["w13"], d["ws13"], d["w2"], d["ws2"], k)
+    torch.cuda.synchronize()
+    host = dict(T=T, H=H, I=I, E=E, k=k, x=x, logits=logits, w13=w13, ws13=ws13, w2=w2, ws2=ws2,
+                ids=ids.cpu().numpy(), wts=wts.cpu().numpy(), st=st.cpu().numpy(), off=off.cpu().numpy(),
+                row_of=row_of.cpu().numpy(), out=bf16_bits(out), out_layer=bf16_bits(out_layer))
+    dev = dict(d, xq1=xq1, xs1=xs1, h=h, aq=aq, as_=as_, a=a, y2=y2, off=off)
+    yield host, dev
+    del dev, d
+    torch.cuda.empty_cache()
+
+
+def segment_tile_rows(off, bm, rng):
+    """Per expert: rows drawn in every bm-row tile of its segment, plus its
+    first and last row."""
+    rows = []
+    for e in range(len(off) - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        r = {a, b - 1}
+        for t0 in range(a, b, bm):
+            r.add(int(rng.integers(t0, min(b, t0 + bm))))
+        rows.append((e, np.array(sorted(r))))
+    return rows
+
+
+def oracle_rows_pooled(fn, items):
+    """Apply a per-item oracle computation on a thread pool (each call of the
+    unchanged single-threaded oracle works on its own rows)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from gpu_util import host_threads
+    oracle.scale_shape(1, 1)   # load the library once, before the threads
+    with ThreadPoolExecutor(host_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
+def test_moe_full_size_route(moe_full):
+    host, _ = moe_full
+    ids_r, w_r = oracle.topk_softmax(host["logits"], host["k"])
+    st_r, off_r, row_of_r = oracle.moe_align(ids_r, host["E"])
+    assert np.array_equal(host["ids"], ids_r)
+    np.testing.assert_allclose(host["wts"], w_r, rtol=2e-6, atol=1e-30)
+    assert np.array_equal(host["off"], off_r) and np.array_equal(host["st"], st_r)
+    assert np.array_equal(host["row_of"], row_of_r)
+    assert np.all(np.diff(off_r) > 0), "every expert receives rows"
+
+
+@pytest.mark.parametrize("variant", MOE_VARIANTS)
+def test_moe_full_size_grouped_gemms(moe_full, variant):
+    """w13 on the gathered codes and w2 on the GPU's own SiLU-requantised
+    activations, in each grouped-GEMM kernel, on rows in every tile."""
+    host, dev = moe_full
+    off = host["off"]
+    samples = segment_tile_rows(off, 128, np.random.default_rng(11))
+    xq1, xs1 = dev["xq1"].cpu().numpy(), dev["xs1"].cpu().numpy()
+    aq, as_ = dev["aq"].cpu().numpy(), dev["as_"].cpu().numpy()
+    for e, rows in samples:
+        q_ref, s_ref = oracle.quant_act(host["x"][host["st"][rows]])
+        assert np.array_equal(xq1[rows], q_ref) and np.array_equal(xs1[rows], s_ref)
+    h = bf16_bits(bi8.moe_gemm(dev["xq1"], dev["xs1"], dev["off"], dev["w13"], dev["ws13"], variant=variant))
+    y2 = bf16_bits(bi8.moe_gemm(dev["aq"], dev["as_"], dev["off"], dev["w2"], dev["ws2"], variant=variant))
+    assert np.all(np.isfinite(bits_to_f64(h))) and np.all(np.isfinite(bits_to_f64(y2)))
+    if variant is None:   # the layer's own intermediates are the default kernel's
+        assert np.array_equal(h, bf16_bits(dev["h"])) and np.array_equal(y2, bf16_bits(dev["y2"]))
+    refs = oracle_rows_pooled(
+        lambda er: (oracle.gemm(xq1[er[1]], xs1[er[1]], host["w13"][er[0]], host["ws13"][er[0]]),
+                    oracle.gemm(aq[er[1]], as_[er[1]], host["w2"][er[0]], host["ws2"][er[0]])), samples)
+    for (e, rows), (r13, r2) in zip(samples, refs):
+        assert_gemm_close(h[rows], r13, "w13 expert %d variant %s" % (e, variant))
+        assert_gemm_close(y2[rows], r2, "w2 expert %d variant %s" % (e, variant))
+
+
+def test_moe_full_size_silu_and_combine_stagewise(moe_full):
+    host, dev = moe_full
+    rows = np.concatenate([r for _, r in segment_tile_rows(host["off"], 128, np.random.default_rng(12))])
+    h, a = bf16_bits(dev["h"][rows]), bf16_bits(dev["a"][rows])
+    assert_bf16_near(a, oracle.silu_mul(h), "silu*up", exact_frac=0.995)
+    q_ref, s_ref = oracle.quant_act(a)
+    assert np.array_equal(dev["aq"][rows].cpu().numpy(), q_ref)
+    assert np.array_equal(dev["as_"][rows].cpu().numpy(), s_ref)
+    tokens = np.random.default_rng(13).choice(host["T"], 256, replace=False)
+    y2 = bf16_bits(dev["y2"])
+    ro = host["row_of"][tokens]
+    wn = host["wts"][tokens]
+    ref = oracle.combine(y2, ro, wn)
+    out = host["out"][tokens]
+    # the fp32 bound of the combine, as in test_combine_stagewise
+    g, r = bits_to_f64(out), bits_to_f64(ref)
+    mag = np.abs(wn[:, :, None].astype(np.float64) * bits_to_f64(y2)[ro]).sum(axis=1)
+    ulp = np.abs(r) * 2.0 ** -7 + 2.0 ** -133
+    assert np.all(np.abs(g - r) <= ulp + host["k"] * 2.0 ** -23 * mag), "combine outside the fp32 bound"
+    assert np.mean(out == ref) >= 0.99
+
+
+def test_moe_full_size_layer_end_to_end(moe_full):
+    """64 tokens, 8 routed to each expert, through the oracle's whole pipeline
+    (route, quantise, w13, SiLU gating, requantise, w2, combine) from the
+    inputs alone, against the GPU layer's output rows."""
+    host, _ = moe_full
+    k, E = host["k"], host["E"]
+    ids_r, w_r = oracle.topk_softmax(host["logits"], k)
+    rng = np.random.default_rng(14)
+    tokens = []
+    for e in range(E):
+        cand = np.setdiff1d(np.nonzero(np.any(ids_r == e, axis=1))[0], tokens)
+        tokens.extend(int(t) for t in rng.choice(cand, 8, replace=False))
+    tokens = np.array(sorted(tokens))
+    assert len(tokens) == 64 and set(ids_r[tokens].reshape(-1)) == set(range(E))
+
+    def one_token(t):
+        q, s = oracle.quant_act(host["x"][t:t + 1])
+        rows = []
+        for slot in range(k):
+            e = int(ids_r[t, slot])
+            hh = oracle.gemm(q, s, host["w13"][e], host["ws13"][e])
+            aq, as_ = oracle.quant_act(oracle.silu_mul(hh))
+            rows.append(oracle.gemm(aq, as_, host["w2"][e], host["ws2"][e])[0])
+        return oracle.combine(np.stack(rows), np.arange(k, dtype=np.int32)[None, :],
+                              w_r[t:t + 1].astype(np.float32))[0]
+
+    ref = np.stack(oracle_rows_pooled(one_token, tokens))
+    got = host["out"][tokens]
+    assert np.all(np.isfinite(bits_to_f64(host["out"]))), "non-finite layer output"
+    rel, frac_gt1, _ = gemm_report(got, ref)
+    assert rel <= GEMM_REL_TOL, "moe layer: max rel err %.3e" % rel
+    assert frac_gt1 <= 0.05, "moe layer: %.3f%% of outputs more than 1 ulp apart" % (100 * frac_gt1)
+    # the one-call layer runs the same kernels: bit-identical
+    assert np.array_equal(host["out_layer"], host["out"])
