@@ -317,14 +317,17 @@ def capture(fn, steps):
 class ClockProbe:
     """Average GFX clock over a timed region, from the shader-clock counters.
 
-    ``libbi8clock.so`` launches a few one-wave workgroups that record the
+    ``libbi8clock.so`` launches one-wave workgroups that record the
     shader-clock cycle counter, the constant-rate real-time counter and the
-    XCD they ran on.  One launch before and one after the region, on the same
-    stream, give per XCD: cycles / real time = the average clock over the
-    region (the launches bracket it, so the figure includes the few
-    microseconds of launch gaps at its ends)."""
+    compute unit they ran on.  One launch before and one after the region, on
+    the same stream, give per compute unit: cycles / real time = the average
+    clock there over the region (the launches bracket it, so the figure
+    includes the few microseconds of launch gaps at its ends).  The cycle
+    counters of different compute units do not agree with each other, so
+    only samples of the same unit are compared; the XCD's figure is the
+    median over its units."""
 
-    BLOCKS = 64   # dispatched round-robin over the XCDs: several per XCD
+    BLOCKS = 1024   # about four per compute unit: every unit is sampled
 
     def __init__(self):
         path = os.path.join(ROOT, "block_wise_int8_amd", "libbi8clock.so")
@@ -342,30 +345,64 @@ class ClockProbe:
         if rc != 0:
             raise RuntimeError("clock probe launch failed (%d)" % rc)
 
+    @staticmethod
+    def _units(sample):
+        """{(xcd, CU / shader array / engine bits of HW_ID): (cycles, real time)}, first sample of each."""
+        out = {}
+        for t, r, place in sample.tolist():
+            key = (place & 0xF, (place >> 40) & 0xFF)
+            out.setdefault(key, (t, r))
+        return out
+
     def read(self):
-        """{"mhz": mean over XCDs, "min", "max", "xcds"} after both marks, or None."""
+        """{"mhz": mean over XCDs, "min", "max" over XCDs, "xcds", "cus"} after both marks, or None."""
         if self.rate_khz <= 0:
             return None
         b = self.buf.cpu().numpy()
-        per_xcd = []
-        for x in sorted(set(b[0, :, 2].tolist()) & set(b[1, :, 2].tolist())):
-            i0 = np.nonzero(b[0, :, 2] == x)[0][0]
-            i1 = np.nonzero(b[1, :, 2] == x)[0][0]
-            dt, dr = b[1, i1, 0] - b[0, i0, 0], b[1, i1, 1] - b[0, i0, 1]
+        u0, u1 = self._units(b[0]), self._units(b[1])
+        per_xcd = {}
+        for key in sorted(set(u0) & set(u1)):
+            dt, dr = u1[key][0] - u0[key][0], u1[key][1] - u0[key][1]
             if dt > 0 and dr > 0:
-                per_xcd.append(dt / dr * self.rate_khz / 1e3)
+                per_xcd.setdefault(key[0], []).append(dt / dr * self.rate_khz / 1e3)
         if not per_xcd:
             return None
-        f = np.array(per_xcd)
+        f = np.array([np.median(v) for v in per_xcd.values()])
         if not (100.0 <= f.mean() <= 4000.0):   # not a shader clock: do not report it
             return None
         return {"mhz": round(float(f.mean()), 1), "min": round(float(f.min()), 1),
-                "max": round(float(f.max()), 1), "xcds": len(f)}
+                "max": round(float(f.max()), 1), "xcds": len(f),
+                "cus": int(sum(len(v) for v in per_xcd.values()))}
 
 
-def timed(fn, steps, use_graph, clock=None):
-    """Run ``steps`` calls of fn; return (wall seconds, event seconds, clock)."""
+SETTLE_S = 0.05   # untimed GPU work before each timed region (see timed)
+
+
+def timed(fn, steps, use_graph, clock=None, warmup=0):
+    """Run ``steps`` calls of fn; return (wall seconds, event seconds, clock).
+
+    Before the timed region the captured steps are replayed, untimed, for at
+    least SETTLE_S seconds, then ``warmup`` untimed calls run right before
+    it.  The GPU idles while a graph is captured and its clock drops; it takes
+    some tens of milliseconds of back-to-back work to settle again (measured
+    at 4096^3: 93-94 us per GEMM with no untimed launches before the region,
+    88-89 us after 20, 84 us after 200 or more), so without the settling the
+    timed region would measure the clock's ramp, not the kernels."""
     g = capture(fn, steps) if use_graph else None
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(steps):
+                fn(i)
+        torch.cuda.synchronize()
+    if warmup:
+        if use_graph:   # back to back on the GPU, as the timed steps run
+            capture(fn, warmup).replay()
+        else:
+            for i in range(warmup):
+                fn(i)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -485,26 +522,26 @@ def main():
     use_graph = not args.eager
     clock = ClockProbe()
 
-    log("[bench] warmup %d steps" % args.warmup)
-    for i in range(args.warmup):
-        w.step(i)
-    torch.cuda.synchronize()
-
-    log("[bench] timing %d steps (%s)" % (args.steps, "graph" if use_graph else "eager"))
-    wall, ev, clk_step = timed(w.step, args.steps, use_graph, clock)
+    # the W warmup steps run right before the timed steps (after the graph
+    # capture, which leaves the GPU idle, and after SETTLE_S of untimed
+    # replays that let the GFX clock settle); every other timed region below
+    # gets the same untimed work of its own right before it
+    log("[bench] timing %d steps (%s) after %d warmup steps" %
+        (args.steps, "graph" if use_graph else "eager", args.warmup))
+    wall, ev, clk_step = timed(w.step, args.steps, use_graph, clock, warmup=args.warmup)
     ms_per_step = wall / args.steps * 1e3
 
     log("[bench] timing the dominant kernel (%s) alone" % w.dominant)
-    _, ev_dom, clk_dom = timed(w.dominant_launch, args.steps, use_graph, clock)
+    _, ev_dom, clk_dom = timed(w.dominant_launch, args.steps, use_graph, clock, warmup=args.warmup)
     t_dom = ev_dom / args.steps
-    _, ev_q, _ = timed(w.quant, args.steps, use_graph)
+    _, ev_q, _ = timed(w.quant, args.steps, use_graph, warmup=args.warmup)
     t_q = ev_q / args.steps
 
     parts = None
     if hasattr(w, "parts"):
         parts = {}
         for name, (fn, nbytes) in w.parts().items():
-            _, ev_p, _ = timed(fn, args.steps, use_graph)
+            _, ev_p, _ = timed(fn, args.steps, use_graph, warmup=args.warmup)
             t_p = ev_p / args.steps
             parts[name] = {"avg_launch_us": round(t_p * 1e6, 3), "GB/s": round(nbytes / t_p / 1e9, 1)}
     value = w.ops / (wall / args.steps) / 1e12
@@ -519,10 +556,8 @@ def main():
         for name in [n for n in args.other.split(",") if n]:
             log("[bench] timing the dominant kernel of %s alone" % name)
             o = make_workload(name)
-            for i in range(min(args.warmup, 10)):
-                o.step(i)
             o.quant(0)
-            _, ev_o, clk_o = timed(o.dominant_launch, args.steps, use_graph, clock)
+            _, ev_o, clk_o = timed(o.dominant_launch, args.steps, use_graph, clock, warmup=args.warmup)
             r = roofline(o, ev_o / args.steps, clk_o)
             r["traffic"] = counter_traffic(name)
             r["config"] = o.config()
@@ -532,7 +567,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "settle_ms": round(SETTLE_S * 1e3),
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic", "config": w.config(), "roofline": roof,
         "roofline_other": others,

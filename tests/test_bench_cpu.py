@@ -97,19 +97,29 @@ class _FakeBuf:
         return self.a
 
 
-def test_clock_probe_reads_cycles_over_real_time_per_xcd():
-    """Two samples per XCD: cycles / real-time ticks * tick rate = clock."""
+def test_clock_probe_reads_cycles_over_real_time_per_unit():
+    """Two samples per compute unit: cycles / real-time ticks * tick rate =
+    clock; units are matched by XCD and HW_ID bits [15:8], the XCD's figure
+    is the median over its units."""
     import numpy as np
     p = bench.ClockProbe.__new__(bench.ClockProbe)
     p.rate_khz = 100000   # 100 MHz real-time counter
-    b = np.zeros((2, 4, 3), np.int64)
-    # XCD 0 at 2000 MHz (20 cycles per tick), XCD 1 at 2200 MHz; the second
-    # sample lists the XCDs in another order, as a later launch may
-    b[0] = [[1000, 500, 0], [7000, 501, 1], [1010, 502, 0], [7005, 503, 1]]
-    b[1] = [[7000 + 22 * 1000, 1501, 1], [1000 + 20 * 1000, 1500, 0], [0, 0, 1], [0, 0, 0]]
+
+    def place(xcd, cu):
+        return (cu << 40) | (0x3 << 32) | xcd   # wave / SIMD bits (low HW_ID bits) are ignored
+
+    b = np.zeros((2, 5, 3), np.int64)
+    # XCD 0: two units at 2000 MHz (20 cycles per tick) with unrelated counter
+    # origins; XCD 1: one unit at 2200 MHz; the second sample lists them in
+    # another order, and a unit seen only once is ignored
+    b[0] = [[1000, 500, place(0, 1)], [9_000_000, 500, place(0, 2)], [7000, 501, place(1, 1)],
+            [1010, 502, place(0, 1)], [5, 5, place(1, 9)]]
+    b[1] = [[7000 + 22 * 1000, 1501, place(1, 1)], [1000 + 20 * 1000, 1500, place(0, 1)],
+            [9_000_000 + 20 * 2000, 2500, place(0, 2)], [0, 0, place(0, 7)], [0, 0, place(0, 1)]]
     p.buf = _FakeBuf(b)
     r = p.read()
-    assert r["xcds"] == 2 and r["min"] == 2000.0 and r["max"] == 2200.0 and r["mhz"] == 2100.0
+    assert r["xcds"] == 2 and r["cus"] == 3
+    assert r["min"] == 2000.0 and r["max"] == 2200.0 and r["mhz"] == 2100.0
     p.rate_khz = 0
     assert p.read() is None
 
