@@ -27,11 +27,13 @@ import os
 import torch
 
 __all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "moe_gemm",
-           "linear", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
+           "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
            "silu_mul_quant", "moe_combine", "moe_layer", "quant_weight", "check_tp_partition", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
            "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
 
 BLOCK = 128
+# size of the library's static workspace behind linear_noalloc (BI8_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 20 << 20
 # kernel variant ids (BI8_GEMM_* in the C header)
 GEMM_AUTO, GEMM_SKINNY, GEMM_TILE_128X64, GEMM_TILE_256X128, GEMM_TILE_256X256 = range(5)
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +80,7 @@ def load() -> ctypes.CDLL:
     lib.blockint8_gemm_variant.argtypes = [i32] + lib.blockint8_gemm.argtypes
     lib.blockint8_moe_gemm_variant.argtypes = [i32] + lib.blockint8_moe_gemm.argtypes
     lib.blockint8_linear.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
+    lib.blockint8_linear_noalloc.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     lib.blockint8_moe_route.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.blockint8_quant_weight.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp]
     lib.blockint8_check_tp_partition.argtypes = [i64, i64, vp, i32, i32, i32, i32]
@@ -85,6 +88,7 @@ def load() -> ctypes.CDLL:
     lib.blockint8_silu_mul_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     lib.blockint8_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, vp]
     for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_linear",
+              "blockint8_linear_noalloc",
               "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_quant_weight",
               "blockint8_check_tp_partition", "blockint8_silu_mul_quant",
               "blockint8_moe_combine", "blockint8_gemm_select",
@@ -282,6 +286,43 @@ def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tenso
     ldx = x.stride(0) if M > 1 else K
     _check(load().blockint8_linear(_ptr(x), ldx, _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K,
                                    block[0], block[1], _ptr(xq), _ptr(xs), _stream_handle(x.device)))
+    return y
+
+
+def linear_noalloc(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tensor | None = None,
+                   y: torch.Tensor | None = None, block=(BLOCK, BLOCK)) -> torch.Tensor:
+    """``linear`` with the quantised activations staged in the library's fixed
+    per-GPU workspace (``NOALLOC_SCRATCH_BYTES``) instead of caller-given
+    buffers: the C call allocates nothing.  Pass ``y`` to allocate nothing
+    here either.  Calls that overlap in time on one GPU race (one stream is
+    safe)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a 2-D bfloat16 tensor")
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a HIP device; there is no CPU path")
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous (stride(1) == 1)")
+    _need(w, "w", torch.int8, 2)
+    _need(ws, "ws", torch.float32, 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] with K = %d (got %s)" % (K, tuple(w.shape)))
+    NB, KB = scale_shape(N, K, *block)
+    if tuple(ws.shape) != (NB, KB):
+        raise ValueError("ws must be [%d, %d]" % (NB, KB))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must be [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    ldx = x.stride(0) if M > 1 else K
+    _check(load().blockint8_linear_noalloc(_ptr(x), ldx, _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K,
+                                           block[0], block[1], _stream_handle(x.device)))
     return y
 
 

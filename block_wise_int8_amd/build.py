@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG, "libblockint8.so")
 # the benchmark's shader-clock probe, a library of its own (not the product path)
 CLOCK_LIB_PATH = os.path.join(PKG, "libbi8clock.so")
 
-SOURCES = ["abi.cpp", "quant_act.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["abi.cpp", "quant_act.hip", "gemm.hip", "moe.hip", "noalloc.hip"]
 CLOCK_SOURCES = ["clockprobe.hip"]
 ARCH = "gfx950"
 

@@ -97,6 +97,61 @@ int32_t check_gemm_common(const char *fn, const int8_t *xq, const float *xs, con
 
 }  // namespace
 
+namespace bi8 {
+
+int32_t fail_status(int32_t status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int32_t call_status(const char *fn, hipError_t e) { return hip_status(fn, e); }
+
+// Argument checks of the dynamic-scale linear (blockint8_linear and its
+// allocation-free form), workspaces aside.
+int32_t check_linear_args(const char *fn, const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws,
+                          const uint16_t *bias, const uint16_t *y, int64_t M, int64_t N, int64_t K,
+                          int32_t block_n, int32_t block_k) {
+    if (M < 0 || M > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: M = %lld out of range", fn, (long long)M);
+    if (N <= 0 || N > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
+    int32_t s = check_k(fn, K);
+    if (s) return s;
+    if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
+    const bool pc = per_channel(block_n, block_k, K);
+    if (pc && K > kMaxPerChannelK)
+        return fail(BI8_ERR_SHAPE, "%s: per-channel blocks take K <= %lld, got %lld", fn,
+                    (long long)kMaxPerChannelK, (long long)K);
+    if (!pc && (s = check_block(fn, block_n, block_k))) return s;
+    if (M == 0) return BI8_OK;
+    if (!x || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
+    if (!aligned(x, 16) || !aligned(w, 16))
+        return fail(BI8_ERR_ALIGN, "%s: x and w must be 16-byte aligned", fn);
+    if (!aligned(ws, 4)) return fail(BI8_ERR_ALIGN, "%s: ws must be 4-byte aligned", fn);
+    if (!aligned(y, 2) || (bias && !aligned(bias, 2)))
+        return fail(BI8_ERR_ALIGN, "%s: y and bias must be 2-byte aligned", fn);
+    return BI8_OK;
+}
+
+// The two launches of the linear: quantise x into (xq, xs), then the GEMM.
+hipError_t launch_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws, const uint16_t *bias,
+                         uint16_t *y, int64_t M, int64_t N, int64_t K, int32_t block_n, int32_t block_k,
+                         int8_t *xq, float *xs, hipStream_t st) {
+    hipError_t e;
+    if (per_channel(block_n, block_k, K)) {
+        e = launch_quant_act_per_token(x, M, K, ldx, xq, xs, st);
+        if (e == hipSuccess) e = launch_gemm_per_channel(xq, xs, w, ws, bias, y, M, N, K, st);
+    } else {
+        e = launch_quant_act(x, M, K, ldx, xq, xs, st);
+        if (e == hipSuccess) e = launch_gemm(GemmPath::kAuto, xq, xs, w, ws, bias, y, M, N, K, st);
+    }
+    return e;
+}
+
+}  // namespace bi8
+
 extern "C" {
 
 const char *blockint8_status_string(int32_t status) {
@@ -178,39 +233,14 @@ int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
                          int32_t block_n, int32_t block_k, int8_t *xq_workspace,
                          float *xs_workspace, void *stream) {
     static const char fn[] = "blockint8_linear";
-    if (M < 0 || M > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: M = %lld out of range", fn, (long long)M);
-    if (N <= 0 || N > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
-    int32_t s = check_k(fn, K);
+    int32_t s = bi8::check_linear_args(fn, x, ldx, w, ws, bias, y, M, N, K, block_n, block_k);
     if (s) return s;
-    if (ldx < K) return fail(BI8_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
-    const bool pc = per_channel(block_n, block_k, K);
-    if (pc && K > kMaxPerChannelK)
-        return fail(BI8_ERR_SHAPE, "%s: per-channel blocks take K <= %lld, got %lld", fn,
-                    (long long)kMaxPerChannelK, (long long)K);
-    if (!pc && (s = check_block(fn, block_n, block_k))) return s;
     if (M == 0) return ok();
-    if (!x || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
     if (!xq_workspace || !xs_workspace) return fail(BI8_ERR_NULL, "%s: NULL workspace pointer", fn);
-    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
-    if (!aligned(x, 16) || !aligned(w, 16))
-        return fail(BI8_ERR_ALIGN, "%s: x and w must be 16-byte aligned", fn);
-    if (!aligned(ws, 4)) return fail(BI8_ERR_ALIGN, "%s: ws must be 4-byte aligned", fn);
-    if (!aligned(y, 2) || (bias && !aligned(bias, 2)))
-        return fail(BI8_ERR_ALIGN, "%s: y and bias must be 2-byte aligned", fn);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
     if (!aligned(xq_workspace, 16) || !aligned(xs_workspace, 4))
         return fail(BI8_ERR_ALIGN, "%s: xq workspace must be 16-byte and xs workspace 4-byte aligned", fn);
-    hipError_t e;
-    if (pc) {
-        e = bi8::launch_quant_act_per_token(x, M, K, ldx, xq_workspace, xs_workspace, st);
-        if (e == hipSuccess)
-            e = bi8::launch_gemm_per_channel(xq_workspace, xs_workspace, w, ws, bias, y, M, N, K, st);
-    } else {
-        e = bi8::launch_quant_act(x, M, K, ldx, xq_workspace, xs_workspace, st);
-        if (e == hipSuccess)
-            e = bi8::launch_gemm(bi8::GemmPath::kAuto, xq_workspace, xs_workspace, w, ws, bias, y, M, N, K, st);
-    }
-    return hip_status(fn, e);
+    return hip_status(fn, bi8::launch_linear(x, ldx, w, ws, bias, y, M, N, K, block_n, block_k, xq_workspace,
+                                             xs_workspace, static_cast<hipStream_t>(stream)));
 }
 
 int32_t blockint8_moe_gemm_variant(int32_t variant, const int8_t *xq, const float *xs,

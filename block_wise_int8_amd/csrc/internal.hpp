@@ -46,6 +46,17 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
                        const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
 
+// Host-side helpers of the C ABI layer (abi.cpp): the thread-local error
+// message, the linear's argument checks and its two launches.
+int32_t fail_status(int32_t status, const char *fmt, ...);
+int32_t call_status(const char *fn, hipError_t e);
+int32_t check_linear_args(const char *fn, const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws,
+                          const uint16_t *bias, const uint16_t *y, int64_t M, int64_t N, int64_t K,
+                          int32_t block_n, int32_t block_k);
+hipError_t launch_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws, const uint16_t *bias,
+                         uint16_t *y, int64_t M, int64_t N, int64_t K, int32_t block_n, int32_t block_k,
+                         int8_t *xq, float *xs, hipStream_t st);
+
 hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, const int32_t *offsets,
                            const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
                            int64_t K, int32_t E, hipStream_t stream);

@@ -172,6 +172,35 @@ int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
                          float *xs_workspace, void *stream);
 
 /*
+ * blockint8_linear without workspace arguments, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The library
+ * allocates nothing either: the quantised activations and their scales are
+ * staged in a fixed array of BI8_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on every GPU it runs on until the process ends.
+ *
+ *   x, ldx, w, ws, bias, y, M, N, K, block_n, block_k: as blockint8_linear
+ *
+ * Same launches and results as blockint8_linear (y bit-identical).  The
+ * codes [M, K] and scales [M, ceil(K/128)] (per-channel: [M, 1]) must fit:
+ * round_up(M * K, 256) + 4 * M * (number of K groups) <= 20 MiB, e.g. M * K
+ * up to 16 MiB at K >= 256.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents: calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race and give
+ * undefined results; calls on one stream are ordered and safe.  The first
+ * call on a device looks the array's address up on that device (the calling
+ * thread's current device, which must be the device of the pointers).
+ *
+ * Errors: as blockint8_linear; a problem larger than the array ->
+ * BI8_ERR_SHAPE.
+ */
+#define BI8_NOALLOC_SCRATCH_BYTES (20ll << 20)
+
+int32_t blockint8_linear_noalloc(const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws,
+                                 const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                                 int32_t block_n, int32_t block_k, void *stream);
+
+/*
  * Offline block quantisation of a bf16 weight into the int8 + fp32 block
  * scale form that blockint8_gemm consumes (section 1 of the page: only
  * int8-serialised weights are loaded; section 2: one fp32 scale per

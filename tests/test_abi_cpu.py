@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
                           "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm",
-                          "blockint8_linear", "blockint8_moe_route", "blockint8_quant_act_gather",
+                          "blockint8_linear", "blockint8_linear_noalloc", "blockint8_moe_route", "blockint8_quant_act_gather",
                           "blockint8_quant_weight", "blockint8_check_tp_partition",
                           "blockint8_silu_mul_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
                           "blockint8_gemm_variant", "blockint8_moe_gemm_variant"}
@@ -228,6 +228,36 @@ def test_linear_rejects(lib, kw, status):
 
 def test_linear_empty_is_noop(lib):
     assert linear(lib, M=0, x=None, w=None, ws=None, y=None, xq=None, xs=None) == OK
+
+
+def linear_noalloc(lib, x=P16, ldx=256, w=P16, ws=P16, bias=None, y=P16, M=4, N=256, K=256, bn=128, bk=128):
+    return lib.blockint8_linear_noalloc(x, ldx, w, ws, bias, y, M, N, K, bn, bk, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(ws=None), NULL), (dict(y=None), NULL),
+    (dict(M=-1), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(ldx=128), SHAPE),
+    (dict(bk=64), BLOCK), (dict(bn=256), BLOCK),
+    (dict(K=136, ldx=136), ALIGN), (dict(ldx=260), ALIGN), (dict(x=P16 + 8), ALIGN),
+    (dict(w=P16 + 1), ALIGN), (dict(ws=P16 + 2), ALIGN), (dict(y=P_ODD), ALIGN), (dict(bias=P_ODD), ALIGN),
+])
+def test_linear_noalloc_rejects(lib, kw, status):
+    assert linear_noalloc(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_linear_noalloc")
+
+
+def test_linear_noalloc_rejects_problems_larger_than_its_workspace(lib):
+    # K = 4096: codes M * 4096 bytes + scales M * 32 * 4 bytes <= 20 MiB up to M = 4964
+    assert (4964 * 4096 + 4 * 4964 * 32) <= bi8.NOALLOC_SCRATCH_BYTES < 4965 * 4096 + 4 * 4965 * 32
+    assert linear_noalloc(lib, M=4965, K=4096, ldx=4096) == SHAPE
+    msg = lib.blockint8_last_error().decode()
+    assert "workspace" in msg and str(bi8.NOALLOC_SCRATCH_BYTES) in msg
+    # per-channel form: one scale per row
+    assert linear_noalloc(lib, M=(20 << 20) // 1024, K=1024, ldx=1024, bn=1, bk=1024) == SHAPE
+
+
+def test_linear_noalloc_empty_is_noop(lib):
+    assert linear_noalloc(lib, M=0, x=None, w=None, ws=None, y=None) == OK
 
 
 def route(lib, logits=P16, T=16, E=8, k=2, ids=P16, w=P16, st=P16, off=P16, ro=P16):
