@@ -375,7 +375,7 @@ class ClockProbe:
                 "cus": int(sum(len(v) for v in per_xcd.values()))}
 
 
-SETTLE_S = 0.05   # untimed GPU work before each timed region (see timed)
+SETTLE_S = 0.05   # default untimed GPU work before each timed region (see timed)
 
 
 def timed(fn, steps, use_graph, clock=None, warmup=0):
@@ -471,17 +471,21 @@ def counter_traffic(workload):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="moe", choices=sorted(wl.CONFIGS))
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3,
+                    help="untimed replays before each timed region, in ms of wall time (default %(default)g; "
+                         "0 for profiler runs that count every dispatch)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for each cpu_baseline leg (one core, all cores)")
     ap.add_argument("--other", default="decode,prefill",
                     help="with the moe workload, also time the dominant GEMM of these dense workloads "
-                         "(comma-separated; empty for none) under roofline_other")
+                         "(comma-separated; empty or 'none' for none) under roofline_other")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS),
                     help="GEMM kernel (default: the library's shape-based choice)")
@@ -503,6 +507,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 16}), flush=True)
         return
 
+    SETTLE_S = max(0.0, args.settle_ms / 1e3)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the block-wise INT8 linear runs on one GPU's share "
@@ -551,9 +556,10 @@ def main():
                        if args.variant == "auto" and not args.per_channel else None)
 
     others = None
-    if args.workload == "moe" and args.other:
+    other_names = [n for n in args.other.split(",") if n and n != "none"]
+    if args.workload == "moe" and other_names:
         others = {}
-        for name in [n for n in args.other.split(",") if n]:
+        for name in other_names:
             log("[bench] timing the dominant kernel of %s alone" % name)
             o = make_workload(name)
             o.quant(0)
