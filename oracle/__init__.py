@@ -24,12 +24,15 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` with gcc."""
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (with ``sanitize``,
+    under AddressSanitizer and UndefinedBehaviorSanitizer, for the host
+    sanitizer run of the CPU tests)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-g"] if sanitize else []
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-               "-fno-finite-math-only", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+               "-fno-finite-math-only", "-shared", "-fPIC"] + san + ["-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
