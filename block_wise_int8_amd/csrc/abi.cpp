@@ -57,6 +57,14 @@ bool per_channel(int32_t block_n, int32_t block_k, int64_t K) { return block_n =
 int32_t check_k(const char *fn, int64_t K) {
     if (K <= 0 || K > BI8_MAX_K)
         return fail(BI8_ERR_SHAPE, "%s: K = %lld out of range [1, %d]", fn, (long long)K, BI8_MAX_K);
+    return BI8_OK;
+}
+
+// The steps whose kernels move rows in 16-byte pieces only (the grouped GEMM,
+// the SiLU requantisation, the weight quantiser) need K % 16 == 0.
+int32_t check_k16(const char *fn, int64_t K) {
+    int32_t s = check_k(fn, K);
+    if (s) return s;
     if (K % 16 != 0)
         return fail(BI8_ERR_ALIGN, "%s: K = %lld must be a multiple of 16", fn, (long long)K);
     return BI8_OK;
@@ -71,12 +79,12 @@ int32_t hip_status(const char *fn, hipError_t e) {
 // block (1, K) is accepted too).
 int32_t check_gemm_common(const char *fn, const int8_t *xq, const float *xs, const int8_t *w,
                           const float *ws, const uint16_t *y, int64_t rows, int64_t N, int64_t K,
-                          int32_t block_n, int32_t block_k, bool allow_pc = false) {
+                          int32_t block_n, int32_t block_k, bool allow_pc = false, bool need_k16 = false) {
     if (rows < 0 || rows > kMaxRows)
         return fail(BI8_ERR_SHAPE, "%s: row count %lld out of range", fn, (long long)rows);
     if (N <= 0 || N > kMaxRows)
         return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
-    int32_t s = check_k(fn, K);
+    int32_t s = need_k16 ? check_k16(fn, K) : check_k(fn, K);
     if (s) return s;
     if (allow_pc && per_channel(block_n, block_k, K)) {
         if (K > kMaxPerChannelK)
@@ -126,9 +134,8 @@ int32_t check_linear_args(const char *fn, const uint16_t *x, int64_t ldx, const 
     if (!pc && (s = check_block(fn, block_n, block_k))) return s;
     if (M == 0) return BI8_OK;
     if (!x || !w || !ws || !y) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
-    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
-    if (!aligned(x, 16) || !aligned(w, 16))
-        return fail(BI8_ERR_ALIGN, "%s: x and w must be 16-byte aligned", fn);
+    if (!aligned(x, 2)) return fail(BI8_ERR_ALIGN, "%s: x must be 2-byte aligned", fn);
+    if (!aligned(w, 16)) return fail(BI8_ERR_ALIGN, "%s: w must be 16-byte aligned", fn);
     if (!aligned(ws, 4)) return fail(BI8_ERR_ALIGN, "%s: ws must be 4-byte aligned", fn);
     if (!aligned(y, 2) || (bias && !aligned(bias, 2)))
         return fail(BI8_ERR_ALIGN, "%s: y and bias must be 2-byte aligned", fn);
@@ -179,9 +186,8 @@ int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
     if (!per_token && (s = check_block(fn, 128, block_k))) return s;
     if (M == 0) return ok();
     if (!x || !xq || !xs) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
-    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
-    if (!aligned(x, 16) || !aligned(xq, 16))
-        return fail(BI8_ERR_ALIGN, "%s: x and xq must be 16-byte aligned", fn);
+    if (!aligned(x, 2)) return fail(BI8_ERR_ALIGN, "%s: x must be 2-byte aligned", fn);
+    if (!aligned(xq, 16)) return fail(BI8_ERR_ALIGN, "%s: xq must be 16-byte aligned", fn);
     if (!aligned(xs, 4)) return fail(BI8_ERR_ALIGN, "%s: xs must be 4-byte aligned", fn);
     if (per_token)
         return hip_status(fn, bi8::launch_quant_act_per_token(x, M, K, ldx, xq, xs,
@@ -210,6 +216,9 @@ int32_t blockint8_gemm_variant(int32_t variant, const int8_t *xq, const float *x
     const bool pc = per_channel(block_n, block_k, K);
     if (pc && variant != BI8_GEMM_AUTO)
         return fail(BI8_ERR_SHAPE, "%s: the per-channel form has one kernel (variant must be AUTO)", fn);
+    if (K % 16 != 0 && variant != BI8_GEMM_AUTO)
+        return fail(BI8_ERR_ALIGN, "%s: K = %lld is not a multiple of 16; that form has one kernel "
+                    "(variant must be AUTO)", fn, (long long)K);
     if (variant == BI8_GEMM_SKINNY && M > 64)
         return fail(BI8_ERR_SHAPE, "%s: the skinny kernel takes M <= 64, got %lld", fn, (long long)M);
     if (M == 0) return ok();
@@ -251,7 +260,7 @@ int32_t blockint8_moe_gemm_variant(int32_t variant, const int8_t *xq, const floa
     if (variant != BI8_GEMM_AUTO && variant != BI8_GEMM_TILE_256X128 && variant != BI8_GEMM_TILE_256X256)
         return fail(BI8_ERR_SHAPE, "%s: kernel variant %d does not run the grouped GEMM", fn, variant);
     if (E <= 0 || E > 65536) return fail(BI8_ERR_SHAPE, "%s: E = %d out of range [1, 65536]", fn, E);
-    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, R, N, K, block_n, block_k);
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, R, N, K, block_n, block_k, false, true);
     if (s) return s;
     if (R == 0) return ok();
     if (!expert_offsets) return fail(BI8_ERR_NULL, "%s: NULL expert_offsets", fn);
@@ -273,7 +282,7 @@ int32_t blockint8_quant_weight(const uint16_t *w, int64_t N, int64_t K, int64_t 
                                int32_t block_k, int8_t *wq, float *ws, void *stream) {
     static const char fn[] = "blockint8_quant_weight";
     if (N < 0 || N > 65535ll * 128) return fail(BI8_ERR_SHAPE, "%s: N = %lld out of range", fn, (long long)N);
-    int32_t s = check_k(fn, K);
+    int32_t s = check_k16(fn, K);
     if (s) return s;
     if (ldw < K) return fail(BI8_ERR_SHAPE, "%s: ldw = %lld < K = %lld", fn, (long long)ldw, (long long)K);
     if ((s = check_block(fn, block_n, block_k))) return s;
@@ -363,9 +372,8 @@ int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, co
     if ((s = check_block(fn, 128, block_k))) return s;
     if (R == 0) return ok();
     if (!rows || !xq || !xs || (T > 0 && !x)) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
-    if (ldx % 8 != 0) return fail(BI8_ERR_ALIGN, "%s: ldx = %lld must be a multiple of 8", fn, (long long)ldx);
-    if ((x && !aligned(x, 16)) || !aligned(xq, 16))
-        return fail(BI8_ERR_ALIGN, "%s: x and xq must be 16-byte aligned", fn);
+    if (x && !aligned(x, 2)) return fail(BI8_ERR_ALIGN, "%s: x must be 2-byte aligned", fn);
+    if (!aligned(xq, 16)) return fail(BI8_ERR_ALIGN, "%s: xq must be 16-byte aligned", fn);
     if (!aligned(xs, 4) || !aligned(rows, 4)) return fail(BI8_ERR_ALIGN, "%s: xs and rows must be 4-byte aligned", fn);
     return hip_status(fn, bi8::launch_quant_act_gather(x, T, ldx, rows, R, K, xq, xs,
                                                         static_cast<hipStream_t>(stream)));
@@ -375,7 +383,7 @@ int32_t blockint8_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int32_
                                  float *as, uint16_t *a, void *stream) {
     static const char fn[] = "blockint8_silu_mul_quant";
     if (R < 0 || R > kMaxRows) return fail(BI8_ERR_SHAPE, "%s: R = %lld out of range", fn, (long long)R);
-    int32_t s = check_k(fn, I);
+    int32_t s = check_k16(fn, I);
     if (s) return s;
     if ((s = check_block(fn, 128, block_k))) return s;
     if (R == 0) return ok();

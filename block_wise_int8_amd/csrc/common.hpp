@@ -44,6 +44,23 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// Exact int32 -> fp32 of an MFMA block sum without a conversion instruction.
+// A block sum of 128 int8 x int8 products has |d| <= 128^3 = 2^21 < 2^22.
+// The MFMA accumulates it onto kAccBiasBits, the bit pattern of 1.5 * 2^23:
+// for |d| < 2^22 the pattern kAccBiasBits + d is the float 1.5 * 2^23 + d
+// (the exponent field stays that of 2^23 and the mantissa field, 2^22 + d,
+// stays inside [0, 2^23)), and subtracting 1.5 * 2^23 from it is exact
+// (both lie within a factor of two of each other), which leaves exactly
+// float(d).  One v_sub_f32 replaces a v_cvt_f32_i32, which issues slower
+// (measured: about 6 cycles per wave64 instruction against 4).  Kernels take
+// `bias` (= kAccBias) from their arguments, so that it sits in a scalar
+// register: a subtraction with the 32-bit literal in the instruction
+// instead issues slower than the conversion.
+constexpr int32_t kAccBiasBits = 0x4B400000;
+constexpr float kAccBias = 12582912.0f;   // 1.5 * 2^23
+
+__device__ __forceinline__ float biased_acc_to_f32(int32_t r, float bias) { return __int_as_float(r) - bias; }
+
 // One int8 code clamp(rne(x / s), -127, 127) with x / s the IEEE correctly
 // rounded quotient, computed from r = rcp(s), the hardware reciprocal (within
 // 1 ulp of 1 / s), by a single multiply.  y = x * r is then within
@@ -105,6 +122,32 @@ __device__ __forceinline__ float quant_group16(const u32x4 &v, uint32_t &lo, uin
         }
     }
     return s;
+}
+
+// The 8 bf16 values p[0..8) as one 16-byte chunk, of which only the first n
+// are read (values past them are zero: the end of a row); p need only be
+// 2-byte aligned.  One 16-byte load when the chunk is whole and aligned,
+// else 2-byte loads.
+__device__ __forceinline__ u32x4 load_bf16x8_any(const uint16_t *p, int64_t n) {
+    if (n >= 8 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) return *reinterpret_cast<const u32x4 *>(p);
+    u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < n) v[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
+    return v;
+}
+
+// Store the first n (1..8) of the 8 int8 codes in (lo, hi) at dst, with one
+// 8-byte store when all 8 are wanted and dst is 8-byte aligned, else byte by
+// byte (rows of a K that is not a multiple of 8 start at any byte).
+__device__ __forceinline__ void store_codes8(int8_t *dst, uint32_t lo, uint32_t hi, int64_t n) {
+    if (n >= 8 && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < n) dst[j] = (int8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFFu);
 }
 
 // Raw buffer resource over [base, base + num_bytes): loads at offsets past the

@@ -54,6 +54,7 @@ struct GemmArgs {
     int64_t tiles_n;
     int32_t E;
     int32_t wide_store;       // y rows allow 8-byte stores (N % 4 == 0, y 8-byte aligned)
+    float acc_bias;           // kAccBias, kept in a scalar register (see biased_acc_to_f32)
 };
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -66,6 +67,42 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 
 __device__ __forceinline__ i32x4 as_i32x4(u32x4 v) {
     return __builtin_bit_cast(i32x4, v);
+}
+
+// 16 bytes at any byte offset `off` of a buffer whose base is 4-byte aligned:
+// five aligned 4-byte loads (each range-checked on its own, so a dword past
+// the buffer's end reads as zero) and byte shifts.  For rows of a K that is
+// not a multiple of 16, which start at any byte.
+__device__ __forceinline__ u32x4 buf_load16_any(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const uint32_t a = off & ~3u, sh = off & 3u;
+    uint32_t d[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) d[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(a + 4u * i), 0, 0);
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
+    return v;
+}
+
+// Keep the first n bytes of a 16-byte operand fragment (none for n <= 0, all
+// for n >= 16): the part of a fragment that lies past the end of a row.
+__device__ __forceinline__ i32x4 keep_bytes(i32x4 v, int64_t n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t b = n - 4 * i;
+        v[i] = b >= 4 ? v[i] : (b <= 0 ? 0 : (int32_t)((uint32_t)v[i] & ((1u << (8 * b)) - 1u)));
+    }
+    return v;
+}
+
+// Buffer resource for bytes [p, p + n) of a tensor at any byte address: the
+// base rounded down to 4 bytes (delta = p % 4 bytes before p) and the range
+// rounded up to whole dwords (a dword holding a byte of the tensor lies on the
+// same page, so reading all of it is safe).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_any(const int8_t *p, int64_t n, uint32_t &delta) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    delta = (uint32_t)(a & 3u);
+    return make_rsrc(reinterpret_cast<const void *>(a - delta), clamp_bytes((n + delta + 3) & ~(int64_t)3));
 }
 
 // ---------------------------------------------------------------------------
@@ -84,7 +121,11 @@ constexpr int kSkinnyUnroll = 4;
 // MT: 16-token column tiles (1 to 4: M <= 16, 32, 48, 64).  PC: the
 // per-channel form (blocks of 1 x K): the block sums are added unscaled and
 // the token and weight-row scales multiply once, in the store.
-template <int MT, bool PC>
+// ODD: K % 16 != 0.  Rows then start at any byte: operand fragments come
+// from aligned 4-byte loads (buf_load16_any), the activation bytes past K are
+// zeroed (so whatever the weight fragment holds there multiplies zero), and
+// blockIdx.y walks the tokens in chunks of 64, so any M runs.
+template <int MT, bool PC, bool ODD>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs p,
                                                                        int32_t blocks_per_wave) {
     // loads of U K blocks are in flight per wave (fewer with 4 token tiles:
@@ -96,15 +137,23 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
     const int row = lane & 15;    // weight row in the tile, and token column
     const int quad = lane >> 4;   // 32-byte quarter of a 128-wide K block
     const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t m0 = ODD ? (int64_t)blockIdx.y * kSkinnyMaxM : 0;   // first token of this workgroup
+    const int64_t mrows = p.M - m0 < kSkinnyMaxM ? p.M - m0 : kSkinnyMaxM;
     const int64_t K = p.K, KB = p.KB;
 
     // Each range covers only what this workgroup may read (<= 2^31 bytes since
     // K <= 2^23), so kOobOffset always lies past it.
+    const int64_t wrows = p.N - n0 < 16 ? p.N - n0 : 16;
+    uint32_t wd = 0, xd = 0;   // ODD: bytes between the 4-byte aligned range base and the first row
     const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(p.w + n0 * K, clamp_bytes((p.N - n0 < 16 ? p.N - n0 : 16) * K));
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, clamp_bytes(p.M * K));
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs, clamp_bytes(p.M * KB * 4));
+        ODD ? make_rsrc_any(p.w + n0 * K, wrows * K, wd) : make_rsrc(p.w + n0 * K, clamp_bytes(wrows * K));
+    const __amdgpu_buffer_rsrc_t xr =
+        ODD ? make_rsrc_any(p.xq + m0 * K, mrows * K, xd) : make_rsrc(p.xq, clamp_bytes(p.M * K));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + m0 * KB, clamp_bytes(mrows * KB * 4));
     const float *ws_row = p.ws + (n0 / kBlock) * KB;
+    auto load = [&](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+        return as_i32x4(ODD ? buf_load16_any(r, off) : buf_load16(r, off));
+    };
 
     const int64_t b_begin = (int64_t)wave * blocks_per_wave;
     const int64_t b_end = b_begin + blocks_per_wave < KB ? b_begin + blocks_per_wave : KB;
@@ -124,19 +173,22 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
             const bool ok = b < b_end;
             const int64_t kk = b * kBlock + quad * 32;
             const bool in0 = ok && kk < K, in1 = ok && kk + 16 < K;
-            wa[u][0] = as_i32x4(buf_load16(wr, in0 ? (uint32_t)(row * K + kk) : kOobOffset));
-            wa[u][1] = as_i32x4(buf_load16(wr, in1 ? (uint32_t)(row * K + kk + 16) : kOobOffset));
+            wa[u][0] = load(wr, in0 ? (uint32_t)(wd + row * K + kk) : kOobOffset);
+            wa[u][1] = load(wr, in1 ? (uint32_t)(wd + row * K + kk + 16) : kOobOffset);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 // lanes of token columns past M load nothing (zero operands)
-                const int64_t tok = mt * 16 + row;
+                const int64_t tok = mt * 16 + row;   // relative to m0
                 xb[u][mt][0] = i32x4{0, 0, 0, 0};
                 xb[u][mt][1] = i32x4{0, 0, 0, 0};
                 if constexpr (!PC) xsv[u][mt] = 0.f;
-                if (tok < p.M) {
-                    xb[u][mt][0] = as_i32x4(buf_load16(xr, in0 ? (uint32_t)(tok * K + kk) : kOobOffset));
-                    xb[u][mt][1] =
-                        as_i32x4(buf_load16(xr, in1 ? (uint32_t)(tok * K + kk + 16) : kOobOffset));
+                if (tok < mrows) {
+                    xb[u][mt][0] = load(xr, in0 ? (uint32_t)(xd + tok * K + kk) : kOobOffset);
+                    xb[u][mt][1] = load(xr, in1 ? (uint32_t)(xd + tok * K + kk + 16) : kOobOffset);
+                    if constexpr (ODD) {
+                        xb[u][mt][0] = keep_bytes(xb[u][mt][0], K - kk);
+                        xb[u][mt][1] = keep_bytes(xb[u][mt][1], K - kk - 16);
+                    }
                     if constexpr (!PC)
                         xsv[u][mt] = buf_load_f32(sr, ok ? (uint32_t)((tok * KB + b) * 4) : kOobOffset);
                 }
@@ -151,16 +203,17 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][0], xb[u][mt][0],
-                                                                  i32x4{0, 0, 0, 0}, 0, 0, 0);
+                // the block sum, accumulated onto kAccBiasBits (see biased_acc_to_f32)
+                i32x4 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    wa[u][0], xb[u][mt][0], i32x4{kAccBiasBits, kAccBiasBits, kAccBiasBits, kAccBiasBits}, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[u][1], xb[u][mt][1], acc, 0, 0, 0);
                 if constexpr (PC) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) yv[mt][i] += (float)acc[i];
+                    for (int i = 0; i < 4; ++i) yv[mt][i] += biased_acc_to_f32(acc[i], p.acc_bias);
                 } else {
                     const float t = xsv[u][mt] * wsv[u];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) yv[mt][i] = fmaf((float)acc[i], t, yv[mt][i]);
+                    for (int i = 0; i < 4; ++i) yv[mt][i] = fmaf(biased_acc_to_f32(acc[i], p.acc_bias), t, yv[mt][i]);
                 }
             }
         }
@@ -179,11 +232,11 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
         float s = 0.f;
 #pragma unroll
         for (int v = 0; v < kSkinnyWaves; ++v) s += red[v][mt][src][i];
-        const int64_t tok = mt * 16 + c, n = n0 + r;
+        const int64_t tok = m0 + mt * 16 + c, n = n0 + r;
         if (tok < p.M && n < p.N) {
             if constexpr (PC) s *= p.xs[tok] * p.ws[n];
             if (p.bias) s += bf16_bits_to_f32(p.bias[n]);
-            p.y[tok * p.N + n] = (uint16_t)f32_to_bf16_bits(s);
+            p.y[tok * p.N + n] = (uint16_t)(f32x2_to_bf16x2_bits(s, 0.0f) & 0xFFFFu);
         }
     }
 }
@@ -408,9 +461,10 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     const BI8_CONST float *ws_row = reinterpret_cast<const BI8_CONST float *>(
         reinterpret_cast<uintptr_t>(t.ws + nbw * KB));
 
-    i32x16 zero16;
+    // each block sum starts from kAccBiasBits (see biased_acc_to_f32)
+    i32x16 bias16;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) zero16[i] = 0;
+    for (int i = 0; i < 16; ++i) bias16[i] = kAccBiasBits;
     f32x16 y[SA][SB];
 #pragma unroll
     for (int a = 0; a < SA; ++a)
@@ -446,7 +500,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
                 for (int b = 0; b < SB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        wf[a][s], xf[b][s], s == 0 ? zero16 : acc[a][b], 0, 0, 0);
+                        wf[a][s], xf[b][s], s == 0 ? bias16 : acc[a][b], 0, 0, 0);
         // the MFMAs belong to this phase
 #pragma unroll
         for (int a = 0; a < SA; ++a)
@@ -464,7 +518,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
             for (int b = 0; b < SB; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    y[a][b][i] = fmaf((float)acc[a][b][i], tb[b], y[a][b][i]);
+                    y[a][b][i] = fmaf(biased_acc_to_f32(acc[a][b][i], p.acc_bias), tb[b], y[a][b][i]);
         // the rescale belongs to this phase
 #pragma unroll
         for (int a = 0; a < SA; ++a)
@@ -541,14 +595,14 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
                 }
                 if (p.wide_store) {
                     if (n < p.N) {
-                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const uint32_t lo = f32x2_to_bf16x2_bits(v[0], v[1]);
+                        const uint32_t hi2 = f32x2_to_bf16x2_bits(v[2], v[3]);
                         *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(v[e], 0.0f) & 0xFFFFu);
                 }
             }
         }
@@ -675,6 +729,8 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // wait for every outstanding LDS read as well.
     float ws_cur = ws_row[0];
 
+    // (the block sums start from zero here: a bias constant would take 16 of
+    // the registers the 8 sub-tiles' accumulators already fill)
     i32x16 zero16;
 #pragma unroll
     for (int i = 0; i < 16; ++i) zero16[i] = 0;
@@ -794,14 +850,14 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
                 }
                 if (p.wide_store) {
                     if (n < p.N) {
-                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const uint32_t lo = f32x2_to_bf16x2_bits(v[0], v[1]);
+                        const uint32_t hi2 = f32x2_to_bf16x2_bits(v[2], v[3]);
                         *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(v[e], 0.0f) & 0xFFFFu);
                 }
             }
         }
@@ -933,14 +989,14 @@ __global__ __launch_bounds__(512) void gemm_perch_kernel(GemmArgs p) {
                 }
                 if (p.wide_store) {
                     if (n < p.N) {
-                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const uint32_t lo = f32x2_to_bf16x2_bits(v[0], v[1]);
+                        const uint32_t hi2 = f32x2_to_bf16x2_bits(v[2], v[3]);
                         *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(v[e], 0.0f) & 0xFFFFu);
                 }
             }
         }
@@ -1075,14 +1131,14 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_perch_wide_kernel(Gemm
                 }
                 if (p.wide_store) {
                     if (n < p.N) {
-                        const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                        const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        const uint32_t lo = f32x2_to_bf16x2_bits(v[0], v[1]);
+                        const uint32_t hi2 = f32x2_to_bf16x2_bits(v[2], v[3]);
                         *reinterpret_cast<uint2 *>(yrow + n) = make_uint2(lo, hi2);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N) yrow[n + e] = (uint16_t)f32_to_bf16_bits(v[e]);
+                        if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(v[e], 0.0f) & 0xFFFFu);
                 }
             }
         }
@@ -1100,21 +1156,24 @@ template __global__ void gemm_wide_kernel<false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true>(GemmArgs);
 
-// One workgroup per 16 weight rows; 16-token tiles by M.
-template <bool PC>
+// One workgroup per 16 weight rows; 16-token tiles by M.  ODD (K % 16 != 0):
+// the same for every M, in chunks of 64 tokens along the grid's y.
+template <bool PC, bool ODD>
 hipError_t launch_skinny(GemmArgs p, hipStream_t stream) {
     const int64_t tiles = (p.N + 15) / 16;
-    if (tiles > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const int64_t chunks = ODD ? (p.M + kSkinnyMaxM - 1) / kSkinnyMaxM : 1;
+    if (tiles > 0x7FFFFFFFll || chunks > 65535) return hipErrorInvalidValue;
+    if (tiles == 0 || chunks == 0) return hipSuccess;
     const int32_t bpw = (int32_t)((p.KB + kSkinnyWaves - 1) / kSkinnyWaves);
-    const dim3 grid((unsigned)tiles), block(kSkinnyWaves * 64);
+    const dim3 grid((unsigned)tiles, (unsigned)chunks), block(kSkinnyWaves * 64);
     if (p.M <= 16)
-        hipLaunchKernelGGL((gemm_skinny_kernel<1, PC>), grid, block, 0, stream, p, bpw);
+        hipLaunchKernelGGL((gemm_skinny_kernel<1, PC, ODD>), grid, block, 0, stream, p, bpw);
     else if (p.M <= 32)
-        hipLaunchKernelGGL((gemm_skinny_kernel<2, PC>), grid, block, 0, stream, p, bpw);
+        hipLaunchKernelGGL((gemm_skinny_kernel<2, PC, ODD>), grid, block, 0, stream, p, bpw);
     else if (p.M <= 48)
-        hipLaunchKernelGGL((gemm_skinny_kernel<3, PC>), grid, block, 0, stream, p, bpw);
+        hipLaunchKernelGGL((gemm_skinny_kernel<3, PC, ODD>), grid, block, 0, stream, p, bpw);
     else
-        hipLaunchKernelGGL((gemm_skinny_kernel<4, PC>), grid, block, 0, stream, p, bpw);
+        hipLaunchKernelGGL((gemm_skinny_kernel<4, PC, ODD>), grid, block, 0, stream, p, bpw);
     return hipGetLastError();
 }
 
@@ -1156,6 +1215,7 @@ GemmArgs make_args(const int8_t *xq, const float *xs, const int8_t *w, const flo
     p.NB = (N + kBlock - 1) / kBlock;
     p.E = 1;
     p.wide_store = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 7) == 0);
+    p.acc_bias = kAccBias;
     return p;
 }
 
@@ -1198,11 +1258,15 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
                        const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
     GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
+    if (K % 16 != 0) {   // rows at any byte: one kernel for every shape
+        if (path != GemmPath::kAuto) return hipErrorInvalidValue;
+        return launch_skinny<false, true>(p, stream);
+    }
     if (path == GemmPath::kAuto) path = select_gemm_path(M, N, K);
     switch (path) {
         case GemmPath::kSkinny: {
             if (M > kSkinnyMaxM) return hipErrorInvalidValue;
-            return launch_skinny<false>(p, stream);
+            return launch_skinny<false, false>(p, stream);
         }
         case GemmPath::kTile256x256:
             p.tiles_m = (M + 255) / 256;
@@ -1232,7 +1296,8 @@ hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8
                                    hipStream_t stream) {
     GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
     p.NB = N;   // one scale per weight row
-    if (use_skinny(M, N, true)) return launch_skinny<true>(p, stream);
+    if (K % 16 != 0) return launch_skinny<true, true>(p, stream);   // rows at any byte
+    if (use_skinny(M, N, true)) return launch_skinny<true, false>(p, stream);
     if (((M + 255) / 256) * ((N + 255) / 256) >= 256) {
         // enough 256 x 256 tiles to fill the chip
         p.tiles_m = (M + 255) / 256;

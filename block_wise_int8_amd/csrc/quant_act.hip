@@ -28,7 +28,11 @@ constexpr int kQuantWaves = 4;          // waves per workgroup
 // rows[m] of x (src_rows rows); an index outside [0, src_rows) reads zeros.
 // kChunks: 16-byte loads in flight per lane (1 for small problems, where the
 // second chunk's arithmetic would only lengthen the critical path).
-template <int kChunks>
+// ODD: K % 8 != 0 or rows not 16-byte aligned (ldx % 8 != 0, or x itself):
+// a lane's chunk may then cross the end of the row or start anywhere; it is
+// read by load_bf16x8_any (values past K read as zero) and its codes stored
+// byte by byte where the 8-byte store would be unaligned.
+template <int kChunks, bool ODD>
 __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     const uint16_t *__restrict__ x, int64_t K, int64_t ldx, int8_t *__restrict__ xq,
     float *__restrict__ xs, int64_t KB, int64_t waves_per_row, int64_t total_waves,
@@ -40,7 +44,7 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     const int64_t g0 = (wave - m * waves_per_row) * 4 * kChunks + (lane >> 4);
     const int64_t src = rows ? (int64_t)rows[m] : m;
     const bool src_ok = src >= 0 && src < src_rows;
-    // Lane chunk j covers group g0 + 4 j.  K % 16 == 0, so a lane's 8
+    // Lane chunk j covers group g0 + 4 j.  With K % 8 == 0 a lane's 8
     // elements are either all inside the row or all outside; outside lanes
     // contribute zeros, which change no group max.  Both loads are issued
     // before either is used.
@@ -49,7 +53,11 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
     for (int j = 0; j < kChunks; ++j) {
         const int64_t g = g0 + 4 * j, k = g * kBlock + (lane & 15) * 8;
         v[j] = u32x4{0u, 0u, 0u, 0u};
-        if (g < KB && k < K && src_ok) v[j] = *reinterpret_cast<const u32x4 *>(x + src * ldx + k);
+        if constexpr (ODD) {
+            if (g < KB && k < K && src_ok) v[j] = load_bf16x8_any(x + src * ldx + k, K - k);
+        } else {
+            if (g < KB && k < K && src_ok) v[j] = *reinterpret_cast<const u32x4 *>(x + src * ldx + k);
+        }
     }
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
@@ -58,7 +66,10 @@ __global__ __launch_bounds__(kQuantWaves * 64) void quant_act_kernel(
         uint32_t lo, hi;
         const float s = quant_group16(v[j], lo, hi);
         if (!valid) continue;
-        *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
+        if constexpr (ODD)
+            store_codes8(xq + m * K + k, lo, hi, K - k);
+        else
+            *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
         if ((lane & 15) == 0) xs[m * KB + g] = s;
     }
 }
@@ -73,18 +84,23 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_quant_act_gather(const uint16_t *x, int64_t src_rows, int64_t ldx, const int32_t *rows,
                                    int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream) {
     const int64_t KB = (K + kBlock - 1) / kBlock;
-    const bool two = M * KB >= 8192;   // enough groups to fill the chip with two per lane
+    const bool odd = K % 8 != 0 || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(x) & 15u) != 0;
+    const bool two = !odd && M * KB >= 8192;   // enough groups to fill the chip with two per lane
     const int64_t gpw = two ? 8 : 4;   // groups per wave
     const int64_t waves_per_row = (KB + gpw - 1) / gpw;
     const int64_t total_waves = M * waves_per_row;
     const int64_t blocks = (total_waves + kQuantWaves - 1) / kQuantWaves;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
     if (blocks == 0) return hipSuccess;
-    if (two)
-        hipLaunchKernelGGL((quant_act_kernel<2>), dim3((unsigned)blocks), dim3(kQuantWaves * 64), 0, stream,
+    const dim3 grid((unsigned)blocks), block(kQuantWaves * 64);
+    if (odd)
+        hipLaunchKernelGGL((quant_act_kernel<1, true>), grid, block, 0, stream, x, K, ldx, xq, xs, KB,
+                           waves_per_row, total_waves, rows, src_rows);
+    else if (two)
+        hipLaunchKernelGGL((quant_act_kernel<2, false>), grid, block, 0, stream,
                            x, K, ldx, xq, xs, KB, waves_per_row, total_waves, rows, src_rows);
     else
-        hipLaunchKernelGGL((quant_act_kernel<1>), dim3((unsigned)blocks), dim3(kQuantWaves * 64), 0, stream,
+        hipLaunchKernelGGL((quant_act_kernel<1, false>), grid, block, 0, stream,
                            x, K, ldx, xq, xs, KB, waves_per_row, total_waves, rows, src_rows);
     return hipGetLastError();
 }
@@ -184,8 +200,10 @@ namespace {
 
 // kChunks > 0: the row fits in kChunks 16-byte loads per thread (K <=
 // 2048 kChunks), which stay in registers between the two passes; 0: the
-// second pass reads the row again.
-template <int kChunks>
+// second pass reads the row again.  ODD: K % 8 != 0 or rows not 16-byte
+// aligned: chunks read by load_bf16x8_any (values past K read as zero) and
+// codes stored byte by byte where the 8-byte store would be unaligned.
+template <int kChunks, bool ODD>
 __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__restrict__ x, int64_t K,
                                                               int64_t ldx, int8_t *__restrict__ xq,
                                                               float *__restrict__ xs) {
@@ -210,7 +228,8 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) row_max(v[c]);
     } else {
-        for (int64_t k = 8 * t; k < K; k += 8 * 256) row_max(*reinterpret_cast<const u32x4 *>(row + k));
+        for (int64_t k = 8 * t; k < K; k += 8 * 256)
+            row_max(ODD ? load_bf16x8_any(row + k, K - k) : *reinterpret_cast<const u32x4 *>(row + k));
     }
     amax = wave_max64(amax);
     if ((t & 63) == 0) wmax[t >> 6] = amax;
@@ -230,7 +249,10 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
                 hi |= ((uint32_t)quant_code(bf16_bits_to_f32(c[2 + j] >> 16), s, r) & 0xFFu) << (16 * j + 8);
             }
         }
-        *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
+        if constexpr (ODD)
+            store_codes8(xq + m * K + k, lo, hi, K - k);
+        else
+            *reinterpret_cast<uint2 *>(xq + m * K + k) = make_uint2(lo, hi);
     };
     if constexpr (kChunks > 0) {
 #pragma unroll
@@ -239,7 +261,8 @@ __global__ __launch_bounds__(256) void quant_act_token_kernel(const uint16_t *__
             if (k < K) codes(v[c], k);
         }
     } else {
-        for (int64_t k = 8 * t; k < K; k += 8 * 256) codes(*reinterpret_cast<const u32x4 *>(row + k), k);
+        for (int64_t k = 8 * t; k < K; k += 8 * 256)
+            codes(ODD ? load_bf16x8_any(row + k, K - k) : *reinterpret_cast<const u32x4 *>(row + k), k);
     }
 }
 
@@ -250,14 +273,17 @@ hipError_t launch_quant_act_per_token(const uint16_t *x, int64_t M, int64_t K, i
     if (M == 0) return hipSuccess;
     if (M > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const int64_t chunks = (K + 2047) / 2048;   // 16-byte loads per thread
-    if (chunks <= 1)
-        hipLaunchKernelGGL((quant_act_token_kernel<1>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+    const dim3 grid((unsigned)M), block(256);
+    if (K % 8 != 0 || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(x) & 15u) != 0)
+        hipLaunchKernelGGL((quant_act_token_kernel<0, true>), grid, block, 0, stream, x, K, ldx, xq, xs);
+    else if (chunks <= 1)
+        hipLaunchKernelGGL((quant_act_token_kernel<1, false>), grid, block, 0, stream, x, K, ldx, xq, xs);
     else if (chunks <= 2)
-        hipLaunchKernelGGL((quant_act_token_kernel<2>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+        hipLaunchKernelGGL((quant_act_token_kernel<2, false>), grid, block, 0, stream, x, K, ldx, xq, xs);
     else if (chunks <= 4)
-        hipLaunchKernelGGL((quant_act_token_kernel<4>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+        hipLaunchKernelGGL((quant_act_token_kernel<4, false>), grid, block, 0, stream, x, K, ldx, xq, xs);
     else
-        hipLaunchKernelGGL((quant_act_token_kernel<0>), dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, xq, xs);
+        hipLaunchKernelGGL((quant_act_token_kernel<0, false>), grid, block, 0, stream, x, K, ldx, xq, xs);
     return hipGetLastError();
 }
 

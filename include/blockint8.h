@@ -30,8 +30,14 @@
  *   - This library implements the [128, 128] block, the block the pages
  *     describe as the usual one (design rationale item 1); any other positive
  *     block size returns BI8_ERR_BLOCK.
- *   - K must be a multiple of 16 (int8 rows are moved in 16-byte pieces);
- *     N and M are arbitrary.  Empty inputs (M == 0, R == 0) are a no-op.
+ *   - K is any size from 1 (section 2 sizes the scale tensor with a ceiling
+ *     for any input size): the activation quantisation, the GEMM and the
+ *     linear take any K and any row stride.  The kernels move int8 rows in
+ *     16-byte pieces; with K % 16 != 0 the rows start at any byte, and one
+ *     alignment-safe kernel serves every shape (slower than the tiled kernels
+ *     of K % 16 == 0).  The grouped GEMM, the SiLU requantisation and the
+ *     weight quantiser keep K % 16 == 0.  N and M are arbitrary.  Empty
+ *     inputs (M == 0, R == 0) are a no-op.
  */
 #ifndef BLOCKINT8_H_
 #define BLOCKINT8_H_
@@ -65,7 +71,8 @@ const char *blockint8_last_error(void);
  * Dynamic activation quantisation (section 4: per-token scales computed at
  * run time; design rationale item 3: int8 values, fp32 scales).
  *
- *   x   bf16 [M, ldx], the first K columns of each row are quantised
+ *   x   bf16 [M, ldx], the first K columns of each row are quantised (any
+ *       row stride ldx >= K, x 2-byte aligned)
  *   xq  int8 [M, K]                    (output)
  *   xs  fp32 [M, ceil(K / block_k)]    (output)
  *
@@ -83,8 +90,9 @@ const char *blockint8_last_error(void);
  * page's platform matrix), xs then [M, 1].
  *
  * Errors: NULL x/xq/xs (M > 0) -> BI8_ERR_NULL; M < 0, K <= 0, K > BI8_MAX_K,
- * ldx < K -> BI8_ERR_SHAPE; block_k not 128 or K -> BI8_ERR_BLOCK; K % 16,
- * ldx % 8, x / xq not 16-byte aligned, xs not 4-byte aligned -> BI8_ERR_ALIGN.
+ * ldx < K -> BI8_ERR_SHAPE; block_k not 128 or K -> BI8_ERR_BLOCK; x not
+ * 2-byte aligned, xq not 16-byte aligned, xs not 4-byte aligned ->
+ * BI8_ERR_ALIGN.
  */
 int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             int32_t block_k, int8_t *xq, float *xs, void *stream);
@@ -114,8 +122,8 @@ int32_t blockint8_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
  * Errors: NULL xq/xs/w/ws/y (M > 0) -> BI8_ERR_NULL; M < 0, N <= 0, K <= 0,
  * K > BI8_MAX_K (2^17 per-channel) -> BI8_ERR_SHAPE; blocks other than
  * [128, 128] and [1, K] -> BI8_ERR_BLOCK;
- * K % 16, xq / w not 16-byte aligned, xs / ws not 4-byte aligned, y / bias
- * not 2-byte aligned -> BI8_ERR_ALIGN.
+ * xq / w not 16-byte aligned, xs / ws not 4-byte aligned, y / bias not
+ * 2-byte aligned -> BI8_ERR_ALIGN.
  */
 int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
                        const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
@@ -140,8 +148,9 @@ int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const
  * Empty segments are allowed.
  *
  * Errors: as blockint8_gemm; NULL expert_offsets -> BI8_ERR_NULL;
- * E <= 0 or E > 65536, R < 0 -> BI8_ERR_SHAPE; expert_offsets not 4-byte
- * aligned -> BI8_ERR_ALIGN.
+ * E <= 0 or E > 65536, R < 0 -> BI8_ERR_SHAPE; K % 16 != 0 (the grouped
+ * kernels are the tiled ones) or expert_offsets not 4-byte aligned ->
+ * BI8_ERR_ALIGN.
  */
 int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
                            const int8_t *w, const float *ws, uint16_t *y,
@@ -155,7 +164,7 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
  * the int8 weight, its block scales and an optional bias, and with no input
  * scale it computes the per-token activation scales itself.
  *
- *   x             bf16 [M, ldx]; row stride ldx >= K elements, ldx % 8 == 0
+ *   x             bf16 [M, ldx]; row stride ldx >= K elements, 2-byte aligned
  *   w, ws, bias, y, block_n, block_k: as blockint8_gemm
  *   xq_workspace  int8 [M, K]           caller-owned; hold the quantised
  *   xs_workspace  fp32 [M, ceil(K/128)] activations on return
@@ -328,7 +337,8 @@ int32_t blockint8_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_
  * Kernel variants.  blockint8_gemm and blockint8_moe_gemm choose a kernel by
  * shape; the *_variant entry points run a named one instead, with the same
  * arguments, results and errors, so that every kernel can be checked and
- * timed on any shape it accepts.  A variant that cannot run the shape
+ * timed on any shape it accepts.  With K % 16 != 0 a single kernel runs
+ * every shape and only BI8_GEMM_AUTO is accepted (BI8_ERR_ALIGN otherwise).  A variant that cannot run the shape
  * (BI8_GEMM_SKINNY with more than 64 rows, BI8_GEMM_SKINNY or
  * BI8_GEMM_TILE_128X64 for the grouped GEMM) returns BI8_ERR_SHAPE; an
  * unknown variant id returns BI8_ERR_SHAPE.  The per-channel form ([1, K]

@@ -74,7 +74,7 @@ def moe(lib, xq=P16, xs=P16, off=P16, w=P16, ws=P16, y=P16, R=4, N=256, K=256, E
     (dict(M=-1), SHAPE), (dict(K=0), SHAPE), (dict(K=-16), SHAPE), (dict(K=1 << 24, ldx=1 << 24), SHAPE),
     (dict(ldx=128), SHAPE),
     (dict(bk=64), BLOCK), (dict(bk=0), BLOCK), (dict(bk=-128), BLOCK),
-    (dict(K=200, ldx=200), ALIGN), (dict(ldx=260), ALIGN), (dict(x=P_ODD), ALIGN),
+    (dict(x=P_ODD), ALIGN),   # any K and any row stride are accepted; x needs 2-byte alignment
     (dict(xq=P16 + 8), ALIGN), (dict(xs=P16 + 2), ALIGN),
 ])
 def test_quant_rejects(lib, kw, status):
@@ -95,7 +95,7 @@ def test_quant_empty_is_noop(lib):
     (dict(bn=0), BLOCK), (dict(bk=-1), BLOCK), (dict(bn=64), BLOCK), (dict(bk=256), BLOCK),
     (dict(bn=1, bk=128), BLOCK), (dict(bn=1, bk=512), BLOCK),   # (1, K) only with block_k == K
     (dict(bn=1, bk=1 << 18, K=1 << 18), SHAPE),                    # per-channel int32 sums: K <= 2^17
-    (dict(K=4008), ALIGN), (dict(xq=P16 + 4), ALIGN), (dict(w=P16 + 8), ALIGN),
+    (dict(xq=P16 + 4), ALIGN), (dict(w=P16 + 8), ALIGN),
     (dict(xs=P16 + 1), ALIGN), (dict(ws=P16 + 3), ALIGN), (dict(y=P_ODD), ALIGN),
     (dict(bias=P_ODD), ALIGN),
 ])
@@ -186,7 +186,9 @@ def gemm_v(lib, variant, M=4, xq=P16, **kw):
     (bi8.GEMM_SKINNY, 65, {}, SHAPE),                       # skinny takes M <= 64
     (bi8.GEMM_TILE_256X256, 64, dict(xq=None), NULL),
     (bi8.GEMM_TILE_256X128, 64, dict(bk=64), BLOCK),
-    (bi8.GEMM_TILE_128X64, 64, dict(K=72), ALIGN),
+    (bi8.GEMM_TILE_128X64, 64, dict(K=72), ALIGN),          # K % 16 != 0: only AUTO
+    (bi8.GEMM_SKINNY, 8, dict(K=4001), ALIGN),
+    (bi8.GEMM_TILE_256X256, 300, dict(K=17), ALIGN),
 ])
 def test_gemm_variant_rejects(lib, variant, M, kw, status):
     assert gemm_v(lib, variant, M=M, **kw) == status
@@ -217,7 +219,7 @@ def linear(lib, x=P16, ldx=256, w=P16, ws=P16, bias=None, y=P16, M=4, N=256, K=2
     (dict(xq=None), NULL), (dict(xs=None), NULL),
     (dict(M=-1), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(ldx=128), SHAPE),
     (dict(bk=64), BLOCK), (dict(bn=256), BLOCK),
-    (dict(K=136, ldx=136), ALIGN), (dict(ldx=260), ALIGN), (dict(x=P16 + 8), ALIGN),
+    (dict(x=P_ODD), ALIGN),
     (dict(w=P16 + 1), ALIGN), (dict(ws=P16 + 2), ALIGN), (dict(y=P_ODD), ALIGN), (dict(bias=P_ODD), ALIGN),
     (dict(xq=P16 + 4), ALIGN), (dict(xs=P16 + 1), ALIGN),
 ])
@@ -238,7 +240,7 @@ def linear_noalloc(lib, x=P16, ldx=256, w=P16, ws=P16, bias=None, y=P16, M=4, N=
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(ws=None), NULL), (dict(y=None), NULL),
     (dict(M=-1), SHAPE), (dict(N=0), SHAPE), (dict(K=0), SHAPE), (dict(ldx=128), SHAPE),
     (dict(bk=64), BLOCK), (dict(bn=256), BLOCK),
-    (dict(K=136, ldx=136), ALIGN), (dict(ldx=260), ALIGN), (dict(x=P16 + 8), ALIGN),
+    (dict(x=P_ODD), ALIGN),
     (dict(w=P16 + 1), ALIGN), (dict(ws=P16 + 2), ALIGN), (dict(y=P_ODD), ALIGN), (dict(bias=P_ODD), ALIGN),
 ])
 def test_linear_noalloc_rejects(lib, kw, status):
@@ -282,7 +284,7 @@ def gather(lib, x=P16, T=8, ldx=256, rows=P16, R=4, K=256, bk=128, xq=P16, xs=P1
 @pytest.mark.parametrize("kw,status", [
     (dict(rows=None), NULL), (dict(x=None), NULL), (dict(xq=None), NULL),
     (dict(R=-1), SHAPE), (dict(T=-1), SHAPE), (dict(K=0), SHAPE), (dict(ldx=128), SHAPE),
-    (dict(bk=64), BLOCK), (dict(K=200, ldx=200), ALIGN), (dict(rows=P16 + 2), ALIGN), (dict(x=P16 + 8), ALIGN),
+    (dict(bk=64), BLOCK), (dict(rows=P16 + 2), ALIGN), (dict(x=P_ODD), ALIGN),
 ])
 def test_quant_act_gather_rejects(lib, kw, status):
     assert gather(lib, **kw) == status

@@ -255,6 +255,25 @@ def test_gemm_power_of_two_bit_exact(M, N, K):
     assert np.array_equal(y, oracle.gemm(xq, xs, w, ws))
 
 
+@pytest.mark.parametrize("variant", [bi8.GEMM_SKINNY] + TILED)
+def test_gemm_subnormal_outputs_bit_exact(variant):
+    """Outputs in the fp32 and bf16 subnormal range, through every kernel: with
+    activation scales 2^-75 or 2^-76 and weight scales 2^-70, every product
+    and partial sum is a multiple of 2^-146 below 2^-123 (at most 23
+    significant bits), so the fp32 sums are exact in any order and the only
+    rounding is the one to bf16 (subnormals kept, ties to even)."""
+    rng = np.random.default_rng(77)
+    M, N, K = 40, 300, 528
+    NB, KB = oracle.scale_shape(N, K)
+    xq = rng.integers(-31, 32, (M, K), dtype=np.int8)
+    w = wl.weights(rng, N, K)
+    xs = np.exp2(rng.choice([-75, -76], (M, KB))).astype(np.float32)
+    ws = np.full((NB, KB), 2.0 ** -70, np.float32)
+    ref = oracle.gemm(xq, xs, w, ws)
+    assert np.mean((ref & 0x7F80) == 0) > 0.3, "the case must reach bf16 subnormals"
+    assert np.array_equal(run_gemm(xq, xs, w, ws, variant=variant), ref)
+
+
 @pytest.mark.parametrize("M", [4, 96])
 def test_gemm_bias(M):
     N, K = 384, 256
