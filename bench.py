@@ -108,6 +108,9 @@ class Dense:
         self.xq = torch.empty((self.M, self.K), dtype=torch.int8, device="cuda")
         self.xs = torch.empty((self.M, KB), dtype=torch.float32, device="cuda")
         self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
+        # the GEMM's caller workspace (split K on grids of few tiles), allocated once
+        nws = 0 if per_channel or variant is not None else bi8.gemm_workspace_size(self.M, self.N, self.K)
+        self.workspace = torch.empty((nws,), dtype=torch.uint8, device="cuda") if nws else None
         self.ops = 2 * self.M * self.N * self.K
         self.quant_shape = (self.M, self.K)
         self.dominant = "gemm_per_channel" if per_channel else "gemm"
@@ -124,7 +127,10 @@ class Dense:
 
     def dominant_launch(self, i):
         j = i % self.copies
-        bi8.gemm(self.xq, self.xs, self.w[j], self.ws[j], y=self.y, block=self.block, variant=self.variant)
+        if self.workspace is not None:
+            bi8.gemm_ws(self.xq, self.xs, self.w[j], self.ws[j], self.workspace, y=self.y)
+        else:
+            bi8.gemm(self.xq, self.xs, self.w[j], self.ws[j], y=self.y, block=self.block, variant=self.variant)
 
     def step(self, i):
         self.quant(i)
@@ -132,9 +138,11 @@ class Dense:
 
     def config(self):
         v = bi8.gemm_select(self.M, self.N, self.K) if self.variant is None else self.variant
+        ws_bytes = 0 if self.workspace is None else self.workspace.numel()
         return {"workload": self.workload, "M": self.M, "K": self.K, "N": self.N,
                 "block": list(self.block), "weight_copies": self.copies,
-                "kernel": "per-channel" if self.per_channel else VARIANT_NAMES[v]}
+                "kernel": "per-channel" if self.per_channel else VARIANT_NAMES[v],
+                "split_k": ws_bytes // (4 * self.M * self.N) if ws_bytes else 1}
 
     def cpu_sample(self, budget_s, threads=1):
         """Time the oracle (quant + GEMM) on a bounded sample of token rows.

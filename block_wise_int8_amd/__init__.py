@@ -26,7 +26,8 @@ import os
 
 import torch
 
-__all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "moe_gemm",
+__all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "gemm_ws",
+           "gemm_workspace_size", "moe_gemm",
            "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
            "silu_mul_quant", "moe_combine", "moe_layer", "quant_weight", "check_tp_partition", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
            "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
@@ -75,6 +76,9 @@ def load() -> ctypes.CDLL:
     lib.blockint8_quant_act.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp]
     lib.blockint8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     lib.blockint8_moe_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+    lib.blockint8_gemm_ws.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp]
+    lib.blockint8_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    lib.blockint8_gemm_workspace_size.restype = i64
     lib.blockint8_gemm_select.argtypes = [i64, i64, i64]
     lib.blockint8_moe_gemm_select.argtypes = [i64, i64, i64, i32]
     lib.blockint8_gemm_variant.argtypes = [i32] + lib.blockint8_gemm.argtypes
@@ -87,7 +91,7 @@ def load() -> ctypes.CDLL:
     lib.blockint8_quant_act_gather.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, vp]
     lib.blockint8_silu_mul_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     lib.blockint8_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, vp]
-    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm", "blockint8_linear",
+    for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_gemm_ws", "blockint8_moe_gemm", "blockint8_linear",
               "blockint8_linear_noalloc",
               "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_quant_weight",
               "blockint8_check_tp_partition", "blockint8_silu_mul_quant",
@@ -202,6 +206,46 @@ def gemm(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tensor,
         _check(load().blockint8_gemm(*args))
     else:
         _check(load().blockint8_gemm_variant(int(variant), *args))
+    return y
+
+
+def gemm_workspace_size(M: int, N: int, K: int, block=(BLOCK, BLOCK)) -> int:
+    """Bytes of workspace ``gemm_ws`` uses for an M x N x K problem (0: none)."""
+    return int(load().blockint8_gemm_workspace_size(M, N, K, block[0], block[1]))
+
+
+def gemm_ws(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tensor,
+            workspace: torch.Tensor | None, bias: torch.Tensor | None = None, y: torch.Tensor | None = None,
+            block=(BLOCK, BLOCK)) -> torch.Tensor:
+    """``gemm`` with a caller workspace (any dtype, contiguous, on the device; or
+    None), which lets problems with few tiles split K between workgroups."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    _need(w, "w", torch.int8, 2)
+    _need(ws, "ws", torch.float32, 2)
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] with K = %d (got %s)" % (K, tuple(w.shape)))
+    NB, KB = scale_shape(N, K, *block)
+    if tuple(xs.shape) != (M, KB) or tuple(ws.shape) != (NB, KB):
+        raise ValueError("scale shapes must be xs [M, %d] and ws [%d, %d]" % (KB, NB, KB))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must be [N]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _need(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M, N]")
+    nbytes = 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on a HIP device")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(load().blockint8_gemm_ws(_ptr(xq), _ptr(xs), _ptr(w), _ptr(ws), _ptr(bias), _ptr(y), M, N, K,
+                                    block[0], block[1], _ptr(workspace), nbytes, _stream_handle(xq.device)))
     return y
 
 

@@ -237,6 +237,30 @@ int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const
                                   stream);
 }
 
+int64_t blockint8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t block_n, int32_t block_k) {
+    if (M <= 0 || M > kMaxRows || N <= 0 || N > kMaxRows || K <= 0 || K > BI8_MAX_K) return 0;
+    if (block_n != 128 || block_k != 128) return 0;   // the per-channel form never splits K
+    return bi8::splitk_workspace_bytes(M, N, K);
+}
+
+int32_t blockint8_gemm_ws(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                          const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K, int32_t block_n,
+                          int32_t block_k, void *workspace, int64_t workspace_bytes, void *stream) {
+    static const char fn[] = "blockint8_gemm_ws";
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, M, N, K, block_n, block_k, true);
+    if (s) return s;
+    if (workspace_bytes < 0)
+        return fail(BI8_ERR_SHAPE, "%s: workspace_bytes = %lld < 0", fn, (long long)workspace_bytes);
+    if (M == 0) return ok();
+    if (bias && !aligned(bias, 2)) return fail(BI8_ERR_ALIGN, "%s: bias must be 2-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16)) return fail(BI8_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (per_channel(block_n, block_k, K))
+        return hip_status(fn, bi8::launch_gemm_per_channel(xq, xs, w, ws, bias, y, M, N, K, st));
+    return hip_status(fn, bi8::launch_gemm_ws(xq, xs, w, ws, bias, y, M, N, K, static_cast<float *>(workspace),
+                                              workspace ? workspace_bytes : 0, st));
+}
+
 int32_t blockint8_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const float *ws,
                          const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
                          int32_t block_n, int32_t block_k, int8_t *xq_workspace,

@@ -55,6 +55,8 @@ struct GemmArgs {
     int32_t E;
     int32_t wide_store;       // y rows allow 8-byte stores (N % 4 == 0, y 8-byte aligned)
     float acc_bias;           // kAccBias, kept in a scalar register (see biased_acc_to_f32)
+    float *partial;           // split K: fp32 partial sums [splits, M, N] (workspace)
+    int64_t kb_per_split;     // split K: K blocks per split (the last split may hold fewer)
 };
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -285,6 +287,22 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
 // m-tiles for one n-tile, then the next n-tile (measured: 8 for the 256 x 128
 // tile, 4 for 256 x 256, where 8 was 15 % slower at 4096^3)
 constexpr int64_t kGroupM = 8;
+
+// Split K: target workgroups on the chip (about two per CU, each 128 x 64
+// tile with a 3-stage ring taking 76 KB of LDS) and the ring depth.
+#ifndef BI8_SPLITK_TARGET
+#define BI8_SPLITK_TARGET 512
+#endif
+#ifndef BI8_SPLITK_STAGES
+#define BI8_SPLITK_STAGES 3
+#endif
+constexpr int64_t kSplitKTarget = BI8_SPLITK_TARGET;
+// The fp32 partials cost splits x M x N x 4 bytes written and read again; on
+// larger outputs that traffic outweighs the shorter K runs (measured: 333 x
+// 5000 x 4000 and 40 x 28672 x 4096 slower split, 64 x 8192 x 4096 and
+// 129 x 1000 x 3088 20-25 % faster).
+constexpr int64_t kSplitKMaxOutputs = 640 * 1024;
+constexpr int kSplitKStages = BI8_SPLITK_STAGES;
 constexpr int64_t kGroupMWide = 4;
 
 struct Tile {
@@ -339,7 +357,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
 // barriers; between them one group issues its MFMAs while the other converts
 // and rescales its previous block (VALU), so each SIMD keeps its matrix core
 // and its vector ALU busy at the same time.
-template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS>
+// SPLIT: split K.  Workgroup (tile, blockIdx.y) sums only the K blocks
+// [blockIdx.y * kb_per_split, + kb_per_split) and stores its fp32 partial sums
+// (no bias, no rounding) in p.partial[blockIdx.y]; splitk_reduce_kernel adds
+// the splits up.  The ring and the scale batches count blocks from the first
+// one of the split.
+template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS, bool SPLIT>
 __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     // (device pass only: the body's address-space casts are not valid host
@@ -368,14 +391,18 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t K = p.K, KB = p.KB;
+    const int64_t K = p.K;
+    // K blocks of this workgroup: [kb0, kb0 + KB); chunks at or past kend read zero
+    const int64_t kb0 = SPLIT ? (int64_t)blockIdx.y * p.kb_per_split : 0;
+    const int64_t KB = SPLIT ? (p.KB - kb0 < p.kb_per_split ? p.KB - kb0 : p.kb_per_split) : p.KB;
+    const int64_t kend = SPLIT ? ((kb0 + KB) * kBlock < K ? (kb0 + KB) * kBlock : K) : K;
 
     // Each range covers only this tile's rows (<= 2^31 bytes since K <= 2^23),
     // so kOobOffset always lies past it.
     const int64_t wrows = p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * KB, clamp_bytes(t.rows * KB * 4));
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * p.KB, clamp_bytes(t.rows * p.KB * 4));
 
     // Per-lane load descriptors.  Load piece q (1 KB) covers tile rows
     // [8q, 8q+8); lane i lands at LDS row 8q + i/8, 16-byte slot i%8, which
@@ -408,27 +435,28 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     // prefetch).  With the first block of a scale batch, the batch's scales
     // are loaded into registers (issued first, so they complete with the
     // stage); they are written to LDS one step before the batch is used.
-    auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
-        const int64_t k0 = kb * kBlock;
+    // (lb: the block's index within this workgroup's run; kb0 + lb: in K)
+    auto issue = [&](char *stage, int64_t lb) __attribute__((always_inline)) {
+        const int64_t k0 = (kb0 + lb) * kBlock;
         const uint32_t kofs = (uint32_t)k0;
-        if ((kb & (C::kSB - 1)) == 0) {
+        if ((lb & (C::kSB - 1)) == 0) {
 #pragma unroll
             for (int j = 0; j < C::kScaleLoads; ++j) {
                 const int f = (wave * C::kScaleLoads + j) * 64 + lane;
-                const int64_t g = kb + (f & (C::kSB - 1));
-                sv[j] = buf_load_f32(sr, g < KB ? (uint32_t)(((f / C::kSB) * KB + g) * 4) : kOobOffset);
+                const int64_t g = lb + (f & (C::kSB - 1));
+                sv[j] = buf_load_f32(sr, g < KB ? (uint32_t)(((f / C::kSB) * p.KB + kb0 + g) * 4) : kOobOffset);
             }
         }
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 wr, (BI8_LDS void *)(stage + C::kWOff + (wave + j * C::kWaves) * 1024), 16,
-                (k0 + wchunk[j] < K) ? wgo[j] + kofs : kOobOffset, 0, 0, 0);
+                (k0 + wchunk[j] < kend) ? wgo[j] + kofs : kOobOffset, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < C::kXLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
-                (k0 + xchunk[j] < K) ? xgo[j] + kofs : kOobOffset, 0, 0, 0);
+                (k0 + xchunk[j] < kend) ? xgo[j] + kofs : kOobOffset, 0, 0, 0);
     };
     // Write the scale batch held in registers to LDS buffer `half`, and make it
     // visible before the next barrier.
@@ -455,11 +483,11 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 
     int64_t nbw = (t.n0 + wn * C::kWaveN) / kBlock;
     if (nbw > p.NB - 1) nbw = p.NB - 1;
-    // The wave's weight-scale row, read through the constant address space so
-    // that the wave-uniform loads become scalar loads (the scales are never
-    // written while the kernel runs).
+    // The wave's weight-scale row (from this workgroup's first block), read
+    // through the constant address space so that the wave-uniform loads
+    // become scalar loads (the scales are never written while the kernel runs).
     const BI8_CONST float *ws_row = reinterpret_cast<const BI8_CONST float *>(
-        reinterpret_cast<uintptr_t>(t.ws + nbw * KB));
+        reinterpret_cast<uintptr_t>(t.ws + nbw * p.KB + kb0));
 
     // each block sum starts from kAccBiasBits (see biased_acc_to_f32)
     i32x16 bias16;
@@ -473,12 +501,15 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) y[a][b][i] = 0.f;
 
-    // MFMA phase: the block's int32 sums for the wave's 2 x 2 sub-tiles, plus
-    // the scales the rescale will need (read now: the stage may be refilled
-    // before the rescale runs).
-    i32x16 acc[SA][SB];
-    float xsv[SB], wsv = 0.f;
-    auto mma = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
+    // MFMA phase: the block's int32 sums for the wave's sub-tiles, plus the
+    // scales the rescale will need (read now: the stage may be refilled before
+    // the rescale runs).  Two buffers (buf): without ping-pong, the rescale of
+    // block kb - 1 runs while block kb's MFMAs execute, so it is off the
+    // per-block chain of barrier, fragment reads and MFMAs (with ping-pong
+    // only buffer 0 is used).
+    i32x16 acc[2][SA][SB];
+    float xsv[2][SB], wsv[2] = {0.f, 0.f};
+    auto mma = [&](const char *stage, int64_t kb, const int buf) __attribute__((always_inline)) {
         i32x4 wf[SA][4], xf[SB][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -491,34 +522,34 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int b = 0; b < SB; ++b)
-            xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
-        wsv = ws_row[kb];
+            xsv[buf][b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
+        wsv[buf] = ws_row[kb];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int a = 0; a < SA; ++a)
 #pragma unroll
                 for (int b = 0; b < SB; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        wf[a][s], xf[b][s], s == 0 ? bias16 : acc[a][b], 0, 0, 0);
+                    acc[buf][a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        wf[a][s], xf[b][s], s == 0 ? bias16 : acc[buf][a][b], 0, 0, 0);
         // the MFMAs belong to this phase
 #pragma unroll
         for (int a = 0; a < SA; ++a)
 #pragma unroll
-            for (int b = 0; b < SB; ++b) asm volatile("" : "+v"(acc[a][b]));
+            for (int b = 0; b < SB; ++b) asm volatile("" : "+v"(acc[buf][a][b]));
     };
     // Rescale phase: y += float(acc) * (xs * ws) per sub-tile.
-    auto epi = [&]() __attribute__((always_inline)) {
+    auto epi = [&](const int buf) __attribute__((always_inline)) {
         float tb[SB];
 #pragma unroll
-        for (int b = 0; b < SB; ++b) tb[b] = xsv[b] * wsv;
+        for (int b = 0; b < SB; ++b) tb[b] = xsv[buf][b] * wsv[buf];
 #pragma unroll
         for (int a = 0; a < SA; ++a)
 #pragma unroll
             for (int b = 0; b < SB; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    y[a][b][i] = fmaf(biased_acc_to_f32(acc[a][b][i], p.acc_bias), tb[b], y[a][b][i]);
+                    y[a][b][i] = fmaf(biased_acc_to_f32(acc[buf][a][b][i], p.acc_bias), tb[b], y[a][b][i]);
         // the rescale belongs to this phase
 #pragma unroll
         for (int a = 0; a < SA; ++a)
@@ -537,19 +568,25 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 
     // NS-stage ring: block kb lives in lds[kb % NS]; loads run NS - 1 blocks
     // ahead.  Before the first barrier of step kb, this wave's loads of block
-    // kb are complete.
-    auto step = [&](const int group, char *cur, char *ahead, int64_t kb) __attribute__((always_inline)) {
+    // kb are complete.  Without ping-pong, block kb's sums use buffer kb % 2:
+    // the ring depth is even, so that is the unrolled step's index % 2.
+    static_assert(PING || NS % 2 == 0, "the two accumulator buffers alternate with the ring's steps");
+    auto step = [&](const int group, char *cur, char *ahead, int64_t kb, const int buf)
+                    __attribute__((always_inline)) {
         wait_stage(kb);
         lds_barrier();
         issue(ahead, kb + NS - 1);
-        if (!PING || group == 0) {
-            mma(cur, kb);
-            if (PING) lds_barrier();
-            epi();
-        } else {
-            if (kb > 0) epi();   // block kb - 1
+        if (!PING) {
+            mma(cur, kb, buf);
+            if (kb > 0) epi(buf ^ 1);   // block kb - 1, under block kb's MFMAs
+        } else if (group == 0) {
+            mma(cur, kb, 0);
             lds_barrier();
-            mma(cur, kb);
+            epi(0);
+        } else {
+            if (kb > 0) epi(0);   // block kb - 1
+            lds_barrier();
+            mma(cur, kb, 0);
         }
         // the next block opens a new scale batch: publish it (its loads were
         // issued with block kb + 1's stage, a step ago)
@@ -562,12 +599,18 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
         int64_t kb = 0;
         for (; kb + NS <= KB; kb += NS) {
 #pragma unroll
-            for (int i = 0; i < NS; ++i) step(group, lds(i), lds((i + NS - 1) % NS), kb + i);
+            for (int i = 0; i < NS; ++i) step(group, lds(i), lds((i + NS - 1) % NS), kb + i, i & 1);
         }
 #pragma unroll
         for (int i = 0; i < NS - 1; ++i)
-            if (kb < KB) step(group, lds(i), lds((i + NS - 1) % NS), kb++);
-        if (PING && group == 1) epi();   // the last block
+            if (kb < KB) step(group, lds(i), lds((i + NS - 1) % NS), kb++, i & 1);
+        if (PING && group == 1) epi(0);   // the last block
+        if (!PING) {                      // the last block, in buffer (KB - 1) % 2
+            if ((KB - 1) & 1)
+                epi(1);
+            else
+                epi(0);
+        }
     };
     if (!PING || wm == 0)
         run(0);
@@ -577,6 +620,33 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 
     // Store.  32x32 result layout: lane -> token column (lane & 31); element i
     // -> weight row 8 * (i / 4) + 4 * (lane >> 5) + (i % 4).
+    if constexpr (SPLIT) {
+        // fp32 partial sums of this split, no bias, no rounding
+        float *part = p.partial + (int64_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+            const int64_t ml = wm * C::kWaveM + b * 32 + rr;
+            if (ml >= t.rows) continue;
+            float *prow = part + (t.m0 + ml) * p.N;
+#pragma unroll
+            for (int a = 0; a < SA; ++a) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int64_t n = t.n0 + wn * C::kWaveN + a * 32 + 8 * i4 + 4 * hi;
+                    if (p.wide_store) {
+                        if (n < p.N)
+                            *reinterpret_cast<f32x4 *>(prow + n) =
+                                f32x4{y[a][b][4 * i4], y[a][b][4 * i4 + 1], y[a][b][4 * i4 + 2], y[a][b][4 * i4 + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) prow[n + e] = y[a][b][4 * i4 + e];
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < SB; ++b) {
         const int64_t ml = wm * C::kWaveM + b * 32 + rr;
@@ -1148,10 +1218,12 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_perch_wide_kernel(Gemm
 
 // Explicit instantiations: the host pass must emit a launch stub for every
 // variant launched below.
-template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true, 3>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true, 3>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3>(GemmArgs);
-template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, false, true, 3, false>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true, 3, false>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3, false>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4, false>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4, true>(GemmArgs);
 template __global__ void gemm_wide_kernel<false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true>(GemmArgs);
@@ -1177,15 +1249,42 @@ hipError_t launch_skinny(GemmArgs p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS>
-hipError_t launch_tiled(GemmArgs p, hipStream_t stream) {
+template <int WN, int WM, int SA, int SB, bool MOE, bool PING, int NS, bool SPLIT = false>
+hipError_t launch_tiled(GemmArgs p, hipStream_t stream, int32_t splits = 1) {
     using C = TileCfg<WN, WM, SA, SB>;
     const int64_t total = p.tiles_m * p.tiles_n;
     if (total <= 0) return hipSuccess;
-    if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, SA, SB, MOE, PING, NS>), dim3((unsigned)total), dim3(C::kThreads),
-                       0, stream, p);
+    if (total > 0x7FFFFFFFll || splits < 1 || splits > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_tiled_kernel<WN, WM, SA, SB, MOE, PING, NS, SPLIT>),
+                       dim3((unsigned)total, (unsigned)splits), dim3(C::kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+// y[m, n] = bf16(sum over the splits, in split order, of partial[z, m, n]
+// (+ bias[n])); four outputs of one row per thread when N % 4 == 0.
+template <bool VEC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partial, int32_t splits,
+                                                            int64_t M, int64_t N, const uint16_t *__restrict__ bias,
+                                                            uint16_t *__restrict__ y) {
+    const int64_t MN = M * N;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1);
+    if (i >= MN) return;
+    if constexpr (VEC) {
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(partial + i);
+        for (int32_t z = 1; z < splits; ++z) acc += *reinterpret_cast<const f32x4 *>(partial + z * MN + i);
+        if (bias) {
+            const int64_t n = i % N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += bf16_bits_to_f32(bias[n + e]);
+        }
+        *reinterpret_cast<uint2 *>(y + i) =
+            make_uint2(f32x2_to_bf16x2_bits(acc[0], acc[1]), f32x2_to_bf16x2_bits(acc[2], acc[3]));
+    } else {
+        float acc = partial[i];
+        for (int32_t z = 1; z < splits; ++z) acc += partial[z * MN + i];
+        if (bias) acc += bf16_bits_to_f32(bias[i % N]);
+        y[i] = (uint16_t)(f32x2_to_bf16x2_bits(acc, 0.0f) & 0xFFFFu);
+    }
 }
 
 template <bool MOE>
@@ -1220,6 +1319,29 @@ GemmArgs make_args(const int8_t *xq, const float *xs, const int8_t *w, const flo
 }
 
 }  // namespace
+
+// Split K for grids of few tiles.  A 128 x 64 grid of at most one tile per
+// CU runs one workgroup per CU, walking all of K one block after another at
+// a pace set by latency; splitting K gives each CU several shorter, independent
+// runs.  Only when the problem would take the 128 x 64 kernel with such a
+// grid and K holds at least 8 blocks per split.
+int32_t splitk_splits(int64_t M, int64_t N, int64_t K) {
+    if (K % 16 != 0 || select_gemm_path(M, N, K) != GemmPath::kTile128x64) return 1;
+    const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
+    const int64_t KB = (K + kBlock - 1) / kBlock;
+    if (tiles > 256 || M * N > kSplitKMaxOutputs) return 1;
+    int64_t s = kSplitKTarget / tiles;   // all splits of all tiles in one round
+    if (s > KB / 8) s = KB / 8;
+    if (s > 16) s = 16;
+    if (s < 2) return 1;
+    const int64_t per = (KB + s - 1) / s;
+    return (int32_t)((KB + per - 1) / per);   // no empty split
+}
+
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int32_t s = splitk_splits(M, N, K);
+    return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
 
 // Tile choice: the 256 x 256 kernel moves the fewest bytes per MAC and wins
 // once its tiles fill the 256 CUs (prefill, gate_up); with fewer (down) the
@@ -1289,6 +1411,34 @@ hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const i
         default:
             return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_ws(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                          const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K, float *workspace,
+                          int64_t workspace_bytes, hipStream_t stream) {
+    const int32_t splits = splitk_splits(M, N, K);
+    if (splits < 2 || !workspace || workspace_bytes < splitk_workspace_bytes(M, N, K))
+        return launch_gemm(GemmPath::kAuto, xq, xs, w, ws, bias, y, M, N, K, stream);
+    GemmArgs p = make_args(xq, xs, w, ws, bias, y, M, N, K);
+    p.tiles_m = (M + 63) / 64;
+    p.tiles_n = (N + 127) / 128;
+    p.partial = workspace;
+    p.kb_per_split = (p.KB + splits - 1) / splits;
+    p.wide_store = N % 4 == 0;   // the workspace is 16-byte aligned: fp32 rows take 16-byte stores
+    hipError_t e = kSplitKStages == 4 ? launch_tiled<4, 2, 1, 1, false, false, 4, true>(p, stream, splits)
+                                      : launch_tiled<4, 2, 1, 1, false, true, 3, true>(p, stream, splits);
+    if (e != hipSuccess) return e;
+    const bool vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+    const int64_t threads = vec ? (M * N) / 4 : M * N;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    if (vec)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, workspace, splits,
+                           M, N, bias, y);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, workspace,
+                           splits, M, N, bias, y);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_per_channel(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,

@@ -42,6 +42,13 @@ hipError_t launch_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int8_t
 hipError_t launch_moe_combine(const uint16_t *y2, int64_t R, const int32_t *row_of, const float *w,
                               int64_t T, int32_t k, int64_t H, uint16_t *out, hipStream_t stream);
 
+// Split K on a caller workspace for grids of few tiles (splits 1: no split).
+int32_t splitk_splits(int64_t M, int64_t N, int64_t K);
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_ws(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                          const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K, float *workspace,
+                          int64_t workspace_bytes, hipStream_t stream);
+
 hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const int8_t *w,
                        const float *ws, const uint16_t *bias, uint16_t *y, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);

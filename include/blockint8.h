@@ -130,6 +130,36 @@ int32_t blockint8_gemm(const int8_t *xq, const float *xs, const int8_t *w, const
                        int32_t block_n, int32_t block_k, void *stream);
 
 /*
+ * blockint8_gemm with an optional caller workspace (the library allocates
+ * nothing).  On problems whose grid of tiles is smaller than the chip
+ * (fewer than one 128 x 64 tile per compute unit, e.g. a few hundred tokens),
+ * a workspace lets the K dimension be split between workgroups: each split
+ * sums its own run of K blocks (exact int32 block sums, rescaled in fp32) into
+ * fp32 partial sums in the workspace, and a second launch adds the splits in
+ * a fixed order, adds the bias and rounds to bf16.  Results are deterministic
+ * and equal blockint8_gemm's up to the order of the fp32 additions (exact
+ * where the sums are, e.g. integer or power-of-two cases).
+ *
+ *   workspace        device memory, 16-byte aligned, or NULL; contents need
+ *                    no initialisation and are undefined on return
+ *   workspace_bytes  its size; when it is below
+ *                    blockint8_gemm_workspace_size(M, N, K, ...) (or NULL),
+ *                    the call is exactly blockint8_gemm
+ *
+ * Calls that share one workspace must not overlap in time.
+ * Errors: as blockint8_gemm; workspace_bytes < 0 -> BI8_ERR_SHAPE;
+ * workspace not 16-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_gemm_ws(const int8_t *xq, const float *xs, const int8_t *w, const float *ws,
+                          const uint16_t *bias, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                          int32_t block_n, int32_t block_k, void *workspace, int64_t workspace_bytes,
+                          void *stream);
+
+/* Workspace bytes blockint8_gemm_ws uses for this problem (0: it never splits
+ * K there, e.g. large grids, K % 16 != 0, the per-channel block, bad sizes). */
+int64_t blockint8_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t block_n, int32_t block_k);
+
+/*
  * Grouped (FusedMoE) block-scaled int8 GEMM (section 5: per-expert int8
  * weights with per-expert fp32 block scales on a leading expert axis;
  * section 6: the MoE runner applies the int8 W8A8 block arithmetic per

@@ -37,7 +37,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
-                          "blockint8_quant_act", "blockint8_gemm", "blockint8_moe_gemm",
+                          "blockint8_quant_act", "blockint8_gemm", "blockint8_gemm_ws",
+                          "blockint8_gemm_workspace_size", "blockint8_moe_gemm",
                           "blockint8_linear", "blockint8_linear_noalloc", "blockint8_moe_route", "blockint8_quant_act_gather",
                           "blockint8_quant_weight", "blockint8_check_tp_partition",
                           "blockint8_silu_mul_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
@@ -102,6 +103,36 @@ def test_quant_empty_is_noop(lib):
 def test_gemm_rejects(lib, kw, status):
     assert gemm(lib, **kw) == status
     assert lib.blockint8_last_error().decode().startswith("blockint8_gemm")
+
+
+def gemm_ws_call(lib, xq=P16, xs=P16, w=P16, ws=P16, bias=None, y=P16, M=4, N=256, K=256, bn=128, bk=128,
+                 wsp=P16, nbytes=1 << 20):
+    return lib.blockint8_gemm_ws(xq, xs, w, ws, bias, y, M, N, K, bn, bk, wsp, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xq=None), NULL), (dict(y=None), NULL), (dict(M=-1), SHAPE), (dict(K=0), SHAPE),
+    (dict(nbytes=-1), SHAPE), (dict(bn=64), BLOCK), (dict(xq=P16 + 4), ALIGN), (dict(wsp=P16 + 8), ALIGN),
+    (dict(bias=P_ODD), ALIGN),
+])
+def test_gemm_ws_rejects(lib, kw, status):
+    assert gemm_ws_call(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_gemm_ws")
+
+
+def test_gemm_workspace_size_host_rule(lib):
+    """Split K only for grids of at most one 128 x 64 tile per CU, outputs of at
+    most 640k entries and >= 16 K blocks."""
+    size = lib.blockint8_gemm_workspace_size
+    assert size(64, 8192, 4096, 128, 128) == 4 * 4 * 64 * 8192   # 64 tiles, 32 K blocks: 4 splits
+    assert size(4096, 4096, 4096, 128, 128) == 0      # a full grid: no split
+    assert size(333, 5000, 4000, 128, 128) == 0       # the partials would cost more than they save
+    assert size(8, 4096, 4096, 128, 128) == 0         # the skinny kernel
+    assert size(64, 8192, 1024, 128, 128) == 0        # too few K blocks
+    assert size(64, 8192, 4001, 128, 128) == 0        # K % 16 != 0
+    assert size(64, 8192, 4096, 1, 4096) == 0         # per-channel
+    assert size(0, 5000, 4096, 128, 128) == 0 and size(10, 10, -1, 128, 128) == 0
+    assert gemm_ws_call(lib, M=0, xq=None, xs=None, w=None, ws=None, y=None, wsp=None) == OK
 
 
 def test_gemm_empty_is_noop(lib):

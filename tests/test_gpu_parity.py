@@ -419,3 +419,77 @@ def test_moe_one_expert_equals_dense_gemm(variant):
     y_moe = bf16_bits(bi8.moe_gemm(xq, xs, to_dev(off), to_dev(w), to_dev(ws), variant=variant))
     y_dense = bf16_bits(bi8.gemm(xq, xs, to_dev(w[0]), to_dev(ws[0]), variant=variant))
     assert np.array_equal(y_moe, y_dense)
+
+
+# ------------------------------------------------------------- split K --
+#
+# blockint8_gemm_ws splits K between workgroups on grids of few 128 x 64 tiles
+# with small outputs (fp32 partial sums in the caller workspace, added in
+# split order by a second launch).  The shapes below all split (asserted
+# through the workspace size); larger outputs do not.
+
+SPLIT_SHAPES = [(129, 1000, 3088), (257, 2056, 4000), (64, 8192, 4096), (100, 6000, 8192), (150, 1001, 2048)]
+
+
+def ws_bytes(M, N, K):
+    return bi8.gemm_workspace_size(M, N, K)
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_gemm_ws_split_k_vs_oracle(M, N, K):
+    nws = ws_bytes(M, N, K)
+    assert nws >= 2 * 4 * M * N, "the shape must split K"
+    x, w, ws = make_case((M, N, K, 21), M, N, K)
+    xq, xs = oracle.quant_act(x)
+    wsp = torch.full((nws,), 0xFF, dtype=torch.uint8, device=device())   # garbage: needs no initialisation
+    args = (to_dev(xq), to_dev(xs), to_dev(w), to_dev(ws))
+    y = bf16_bits(bi8.gemm_ws(*args, wsp))
+    rows = tile_rows(0, M, 64, np.random.default_rng(M), per_tile=2)
+    assert_gemm_close(y[rows], oracle_gemm_rows(xq[rows], xs[rows], w, ws), "split K %dx%dx%d" % (M, N, K))
+    assert np.all(np.isfinite(bits_to_f64(y)))
+    # deterministic, and within the tolerance of the unsplit kernel everywhere
+    assert np.array_equal(bf16_bits(bi8.gemm_ws(*args, wsp)), y)
+    assert_gemm_close(y, bf16_bits(bi8.gemm(*args)), "split vs unsplit")
+
+
+def test_gemm_ws_split_k_integer_bit_exact():
+    """Unit scales, |xq| <= 31: every partial sum is an integer below 2^24, so
+    the split sums are exact in any order: y == bf16(int64 matmul)."""
+    M, N, K = 200, 512, 2048
+    assert ws_bytes(M, N, K) > 0
+    rng = np.random.default_rng(4)
+    xq = rng.integers(-31, 32, (M, K), dtype=np.int8)
+    w = wl.weights(rng, N, K)
+    NB, KB = oracle.scale_shape(N, K)
+    wsp = torch.empty((ws_bytes(M, N, K),), dtype=torch.uint8, device=device())
+    y = bf16_bits(bi8.gemm_ws(to_dev(xq), to_dev(np.ones((M, KB), np.float32)), to_dev(w),
+                              to_dev(np.ones((NB, KB), np.float32)), wsp))
+    exact = (xq.astype(np.int64) @ w.astype(np.int64).T).astype(np.float32)
+    assert np.array_equal(y, wl.to_bf16_bits(exact))
+
+
+def test_gemm_ws_bias_odd_n_and_unaligned_y():
+    M, N, K = 150, 1001, 2048
+    nws = ws_bytes(M, N, K)
+    assert nws > 0
+    x, w, ws = make_case(5, M, N, K)
+    bias = wl.activations(np.random.default_rng(6), 1, N)[0]
+    xq, xs = oracle.quant_act(x)
+    wsp = torch.empty((nws,), dtype=torch.uint8, device=device())
+    ybuf = torch.zeros((M * N + 1,), dtype=torch.bfloat16, device=device())
+    y = ybuf[1:].view(M, N)    # 2-byte aligned rows, element-wise stores
+    bi8.gemm_ws(to_dev(xq), to_dev(xs), to_dev(w), to_dev(ws), wsp, bias=bf16_to_dev(bias), y=y)
+    assert_gemm_close(bf16_bits(y), oracle.gemm(xq, xs, w, ws, bias=bias), "split K with bias, N=1001")
+
+
+def test_gemm_ws_small_or_missing_workspace_is_gemm():
+    M, N, K = 257, 2056, 4000
+    x, w, ws = make_case(8, M, N, K)
+    xq, xs = oracle.quant_act(x)
+    args = (to_dev(xq), to_dev(xs), to_dev(w), to_dev(ws))
+    ref = bf16_bits(bi8.gemm(*args))
+    small = torch.empty((ws_bytes(M, N, K) - 16,), dtype=torch.uint8, device=device())
+    assert np.array_equal(bf16_bits(bi8.gemm_ws(*args, small)), ref)
+    assert np.array_equal(bf16_bits(bi8.gemm_ws(*args, None)), ref)
+    # shapes that do not split ignore the workspace
+    assert ws_bytes(4096, 4096, 4096) == 0 and ws_bytes(8, 4096, 4096) == 0 and ws_bytes(333, 5000, 4000) == 0
