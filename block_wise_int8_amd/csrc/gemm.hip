@@ -160,6 +160,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
     const int64_t b_begin = (int64_t)wave * blocks_per_wave;
     const int64_t b_end = b_begin + blocks_per_wave < KB ? b_begin + blocks_per_wave : KB;
 
+    // Weight loads in whole 128-byte lines (K % 16 == 0): load lane l reads
+    // 16-byte chunk l % 8 of tile row l / 8 (and of row 8 + l / 8 with the
+    // second load), so one load instruction covers 8 full lines.  The MFMA's A
+    // operand wants lane (i, q) = (l % 16, l / 16) to hold chunk 2q + m of row
+    // i for MFMA m; cross-lane permutes (ds_bpermute) move each chunk there
+    // from load lane (i % 8) * 8 + 2q + m, of the first or the second load.
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    const int bp0 = ((lane & 7) * 8 + 2 * (lane >> 4)) * 4;   // byte index of the source lane, m = 0
+    const bool upper = (lane & 15) >= 8;                        // MFMA rows 8-15: from the second load
+
     f32x4 yv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) yv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -175,8 +185,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
             const bool ok = b < b_end;
             const int64_t kk = b * kBlock + quad * 32;
             const bool in0 = ok && kk < K, in1 = ok && kk + 16 < K;
-            wa[u][0] = load(wr, in0 ? (uint32_t)(wd + row * K + kk) : kOobOffset);
-            wa[u][1] = load(wr, in1 ? (uint32_t)(wd + row * K + kk + 16) : kOobOffset);
+            if constexpr (ODD) {
+                wa[u][0] = load(wr, in0 ? (uint32_t)(wd + row * K + kk) : kOobOffset);
+                wa[u][1] = load(wr, in1 ? (uint32_t)(wd + row * K + kk + 16) : kOobOffset);
+            } else {   // whole lines; permuted into the MFMA layout below
+                const int64_t kc = b * kBlock + lchunk * 16;
+                const bool inl = ok && kc < K;
+                wa[u][0] = load(wr, inl ? (uint32_t)(lrow * K + kc) : kOobOffset);
+                wa[u][1] = load(wr, inl ? (uint32_t)((lrow + 8) * K + kc) : kOobOffset);
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 // lanes of token columns past M load nothing (zero operands)
@@ -203,6 +220,20 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void gemm_skinny_kernel(GemmArgs
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            if constexpr (!ODD) {
+                i32x4 a0, a1;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const int lo0 = __builtin_amdgcn_ds_bpermute(bp0, wa[u][0][d]);
+                    const int hi0 = __builtin_amdgcn_ds_bpermute(bp0, wa[u][1][d]);
+                    const int lo1 = __builtin_amdgcn_ds_bpermute(bp0 + 4, wa[u][0][d]);
+                    const int hi1 = __builtin_amdgcn_ds_bpermute(bp0 + 4, wa[u][1][d]);
+                    a0[d] = upper ? hi0 : lo0;
+                    a1[d] = upper ? hi1 : lo1;
+                }
+                wa[u][0] = a0;
+                wa[u][1] = a1;
+            }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 // the block sum, accumulated onto kAccBiasBits (see biased_acc_to_f32)
