@@ -184,7 +184,9 @@ class Dense:
 class Moe:
     """The FusedMoE layer on the GPU, one launch per step: route (top-k of the
     softmax of the router logits, dispatch order), gather + quantise, w13
-    grouped GEMM, SiLU gating + requantise, w2 grouped GEMM, weighted combine."""
+    grouped GEMM with SiLU gating + requantise in its epilogue (the two as
+    separate launches when a kernel variant is forced), w2 grouped GEMM,
+    weighted combine."""
 
     def __init__(self, variant=None):
         c = wl.CONFIGS["moe"]
@@ -221,10 +223,13 @@ class Moe:
         self.copies = 1
         self.quant_shape = (self.R, H)   # the gathered rows
         self.ops = 2 * self.R * (2 * I) * H + 2 * self.R * H * I
-        self.dominant = "moe_gemm_w13"
+        self.fused = variant is None and I % 128 == 0
+        self.dominant = "moe_gemm_w13_silu_quant" if self.fused else "moe_gemm_w13"
         self.dominant_ops = 2 * self.R * (2 * I) * H
-        self.dominant_bytes = (self.R * H + 4 * self.R * KB1 + E * 2 * I * H
-                               + 4 * E * bi8.scale_shape(2 * I, H)[0] * KB1 + 2 * self.R * 2 * I)
+        w13_in = self.R * H + 4 * self.R * KB1 + E * 2 * I * H + 4 * E * bi8.scale_shape(2 * I, H)[0] * KB1
+        self.w13_bytes = w13_in + 2 * self.R * 2 * I
+        self.fused_bytes = w13_in + self.R * I + 4 * self.R * KB2
+        self.dominant_bytes = self.fused_bytes if self.fused else self.w13_bytes
         self.workload = ("moe layer T=%d tokens top-%d of E=%d, hidden %d, intermediate %d, "
                          "block [128,128]" % (T, k, E, H, I))
         self.route(0)
@@ -236,14 +241,26 @@ class Moe:
     def quant(self, i):
         bi8.quant_act_gather(self.x, self.st, self.xq1, self.xs1)
 
-    def dominant_launch(self, i):
+    def launch_w13(self, i):
         bi8.moe_gemm(self.xq1, self.xs1, self.off, self.w13, self.ws13, y=self.y13, variant=self.variant)
+
+    def launch_w13_gated(self, i):
+        bi8.moe_gemm_silu_quant(self.xq1, self.xs1, self.off, self.w13, self.ws13, self.xq2, self.xs2)
+
+    def dominant_launch(self, i):
+        if self.fused:
+            self.launch_w13_gated(i)
+        else:
+            self.launch_w13(i)
 
     def step(self, i):
         self.route(i)
         self.quant(i)
-        self.dominant_launch(i)
-        bi8.silu_mul_quant(self.y13, self.xq2, self.xs2)
+        if self.fused:
+            self.launch_w13_gated(i)
+        else:
+            self.launch_w13(i)
+            bi8.silu_mul_quant(self.y13, self.xq2, self.xs2)
         bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2, variant=self.variant)
         bi8.moe_combine(self.y2, self.row_of, self.wts, out=self.out)
 
@@ -254,7 +271,8 @@ class Moe:
         return {
             "route": (self.route, 4 * T * self.E + 4 * T * k * 4 + 4 * (self.E + 1)),
             "gather_quant": (self.quant, quant_bytes(R, H)),
-            "moe_gemm_w13": (self.dominant_launch, self.dominant_bytes),
+            "moe_gemm_w13_silu_quant": (self.launch_w13_gated, self.fused_bytes),
+            "moe_gemm_w13": (self.launch_w13, self.w13_bytes),
             "silu_mul_quant": (lambda i: bi8.silu_mul_quant(self.y13, self.xq2, self.xs2),
                                2 * R * 2 * I + R * I + 4 * R * KB2),
             "moe_gemm_w2": (lambda i: bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2,
@@ -267,9 +285,12 @@ class Moe:
     def config(self):
         v = (bi8.moe_gemm_select(self.R, 2 * self.I, self.H, self.E) if self.variant is None
              else self.variant)
+        v2 = (bi8.moe_gemm_select(self.R, self.H, self.I, self.E) if self.variant is None
+              else self.variant)
         return {"workload": self.workload, "T": self.T, "E": self.E, "topk": self.k,
                 "hidden": self.H, "intermediate": self.I, "rows": self.R, "block": [128, 128],
-                "kernel": VARIANT_NAMES[v]}
+                "kernel": VARIANT_NAMES[v], "kernel_w2": VARIANT_NAMES[v2],
+                "w13_gating_epilogue": self.fused}
 
     def cpu_sample(self, budget_s, threads=1):
         """Time the oracle's layer (route, quantise, w13 GEMM, SiLU, requantise,

@@ -13,8 +13,9 @@ Entry points (same names as the C ABI, without the ``blockint8_`` prefix):
 * :func:`moe_gemm`   -- the same per expert over expert-sorted rows
 * :func:`linear`     -- quant_act followed by gemm (the dynamic-scale linear)
 * :func:`moe_route`, :func:`quant_act_gather`, :func:`silu_mul_quant`,
-  :func:`moe_combine` -- the MoE steps around the grouped GEMM, and
-  :func:`moe_layer`, the whole FusedMoE layer built from them
+  :func:`moe_combine` -- the MoE steps around the grouped GEMM,
+  :func:`moe_gemm_silu_quant` -- the w13 GEMM with the gating as its epilogue,
+  and :func:`moe_layer`, the whole FusedMoE layer built from them
 
 ``gemm`` and ``moe_gemm`` pick a kernel by shape (:func:`gemm_select`,
 :func:`moe_gemm_select`); their ``variant`` argument names one instead.
@@ -29,7 +30,7 @@ import torch
 __all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "gemm_ws",
            "gemm_workspace_size", "moe_gemm",
            "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
-           "silu_mul_quant", "moe_combine", "moe_layer", "quant_weight", "check_tp_partition", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
+           "silu_mul_quant", "moe_gemm_silu_quant", "moe_combine", "moe_layer", "quant_weight", "check_tp_partition", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
            "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
 
 BLOCK = 128
@@ -90,11 +91,12 @@ def load() -> ctypes.CDLL:
     lib.blockint8_check_tp_partition.argtypes = [i64, i64, vp, i32, i32, i32, i32]
     lib.blockint8_quant_act_gather.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, vp]
     lib.blockint8_silu_mul_quant.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    lib.blockint8_moe_gemm_silu_quant.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
     lib.blockint8_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, vp]
     for f in ("blockint8_quant_act", "blockint8_gemm", "blockint8_gemm_ws", "blockint8_moe_gemm", "blockint8_linear",
               "blockint8_linear_noalloc",
               "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_quant_weight",
-              "blockint8_check_tp_partition", "blockint8_silu_mul_quant",
+              "blockint8_check_tp_partition", "blockint8_silu_mul_quant", "blockint8_moe_gemm_silu_quant",
               "blockint8_moe_combine", "blockint8_gemm_select",
               "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant"):
         getattr(lib, f).restype = i32
@@ -443,6 +445,43 @@ def silu_mul_quant(h: torch.Tensor, aq: torch.Tensor | None = None, as_: torch.T
     return (aq, as_, a) if return_a else (aq, as_)
 
 
+def moe_gemm_silu_quant(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w13: torch.Tensor,
+                        ws13: torch.Tensor, aq: torch.Tensor | None = None, as_: torch.Tensor | None = None,
+                        block=(BLOCK, BLOCK)):
+    """The w13 grouped GEMM with the SiLU gating and requantisation as its
+    epilogue: (aq int8 [R, I], as fp32 [R, I/128]), bit-identical to
+    silu_mul_quant(moe_gemm(xq, xs, expert_offsets, w13, ws13)).  w13 is
+    int8 [E, 2I, K] (gate rows, then up rows); I % 128 == 0."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _need(w13, "w13", torch.int8, 3)
+    _need(ws13, "ws13", torch.float32, 3)
+    R, K = xq.shape
+    E, N, Kw = w13.shape
+    if Kw != K or N % 2:
+        raise ValueError("w13 must be [E, 2I, K] with K = %d" % K)
+    I = N // 2
+    if expert_offsets.shape[0] != E + 1:
+        raise ValueError("expert_offsets must have E + 1 = %d entries" % (E + 1))
+    NB, KB = scale_shape(N, K, *block)
+    if tuple(xs.shape) != (R, KB) or tuple(ws13.shape) != (E, NB, KB):
+        raise ValueError("scale shapes must be xs [R, %d] and ws13 [E, %d, %d]" % (KB, NB, KB))
+    IB = (I + block[1] - 1) // block[1]
+    if aq is None:
+        aq = torch.empty((R, I), dtype=torch.int8, device=xq.device)
+    if as_ is None:
+        as_ = torch.empty((R, IB), dtype=torch.float32, device=xq.device)
+    _need(aq, "aq", torch.int8, 2)
+    _need(as_, "as_", torch.float32, 2)
+    if tuple(aq.shape) != (R, I) or tuple(as_.shape) != (R, IB):
+        raise ValueError("aq must be [R, %d] and as_ [R, %d]" % (I, IB))
+    _check(load().blockint8_moe_gemm_silu_quant(_ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(w13), _ptr(ws13),
+                                                _ptr(aq), _ptr(as_), R, I, K, E, block[0], block[1],
+                                                _stream_handle(xq.device)))
+    return aq, as_
+
+
 def moe_combine(y2: torch.Tensor, row_of: torch.Tensor, topk_weights: torch.Tensor,
                 out: torch.Tensor | None = None) -> torch.Tensor:
     """out[t] = bf16(sum_s w[t, s] * y2[row_of[t, s]]) -> bf16 [T, H]."""
@@ -466,12 +505,16 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, ws13: to
               variant: int | None = None):
     """The block-wise INT8 FusedMoE layer on the GPU, one launch per step:
     route, gather + quantise, w13 grouped GEMM, SiLU gating + quantise, w2
-    grouped GEMM, weighted combine.  x bf16 [T, H]; logits fp32 [T, E];
+    grouped GEMM, weighted combine.  With the default kernels and I % 128 == 0
+    the w13 GEMM and the gating run as one launch (moe_gemm_silu_quant).  x bf16 [T, H]; logits fp32 [T, E];
     w13 int8 [E, 2I, H]; w2 int8 [E, H, I].  Returns bf16 [T, H]."""
     ids, w, st, off, row_of = moe_route(logits, k, renormalize)
     xq, xs = quant_act_gather(x, st)
-    h = moe_gemm(xq, xs, off, w13, ws13, variant=variant)
-    aq, as_ = silu_mul_quant(h)
+    if variant is None and (w13.shape[1] // 2) % BLOCK == 0:
+        aq, as_ = moe_gemm_silu_quant(xq, xs, off, w13, ws13)
+    else:
+        h = moe_gemm(xq, xs, off, w13, ws13, variant=variant)
+        aq, as_ = silu_mul_quant(h)
     y2 = moe_gemm(aq, as_, off, w2, ws2, variant=variant)
     return moe_combine(y2, row_of, w)
 

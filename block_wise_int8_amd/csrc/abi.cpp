@@ -403,6 +403,28 @@ int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, co
                                                         static_cast<hipStream_t>(stream)));
 }
 
+int32_t blockint8_moe_gemm_silu_quant(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
+                                      const int8_t *w13, const float *ws13, int8_t *aq, float *as, int64_t R,
+                                      int64_t I, int64_t K, int32_t E, int32_t block_n, int32_t block_k,
+                                      void *stream) {
+    static const char fn[] = "blockint8_moe_gemm_silu_quant";
+    if (E <= 0 || E > 65536) return fail(BI8_ERR_SHAPE, "%s: E = %d out of range [1, 65536]", fn, E);
+    if (I <= 0 || I % 128 != 0 || I > kMaxRows / 2)
+        return fail(BI8_ERR_SHAPE, "%s: I = %lld must be a positive multiple of 128", fn, (long long)I);
+    // a placeholder y: the epilogue writes aq / as, no bf16 output
+    const uint16_t *no_y = reinterpret_cast<const uint16_t *>(aq);
+    int32_t s = check_gemm_common(fn, xq, xs, w13, ws13, no_y, R, 2 * I, K, block_n, block_k, false, true);
+    if (s) return s;
+    if (R == 0) return ok();
+    if (!expert_offsets || !aq || !as) return fail(BI8_ERR_NULL, "%s: NULL tensor pointer", fn);
+    if (!aligned(expert_offsets, 4))
+        return fail(BI8_ERR_ALIGN, "%s: expert_offsets must be 4-byte aligned", fn);
+    if (!aligned(aq, 16)) return fail(BI8_ERR_ALIGN, "%s: aq must be 16-byte aligned", fn);
+    if (!aligned(as, 4)) return fail(BI8_ERR_ALIGN, "%s: as must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_moe_gemm_silu_quant(xq, xs, expert_offsets, w13, ws13, aq, as, R, I, K, E,
+                                                          static_cast<hipStream_t>(stream)));
+}
+
 int32_t blockint8_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int32_t block_k, int8_t *aq,
                                  float *as, uint16_t *a, void *stream) {
     static const char fn[] = "blockint8_silu_mul_quant";

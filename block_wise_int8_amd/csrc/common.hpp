@@ -150,6 +150,23 @@ __device__ __forceinline__ void store_codes8(int8_t *dst, uint32_t lo, uint32_t 
         if (j < n) dst[j] = (int8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFFu);
 }
 
+// silu(g) * u = g / (1 + exp(-g)) * u in fp32, with exp(-g) as the hardware
+// 2^x of -g log2(e) (the rounded argument, |g log2(e)| <= 116 here, moves it
+// by at most 116 * 2^-24 * ln 2 ~ 5e-6 relative; 2^x itself within 1 ulp) and
+// the quotient through the hardware reciprocal (within 1 ulp).  The bf16
+// result then differs from a correctly rounded evaluation's only where the
+// fp32 value sits within ~1e-5 of a bf16 rounding boundary.  Below g = -80,
+// exp(g) nears the fp32 subnormal range
+// (and exp(-g) overflows past g = -88.7, which would give zero where the
+// result is still a normal bf16), so there the product is formed as
+// g * (2^64 exp(g)) * u * 2^-64 with 2^64 exp(g) = exp2(g log2(e) + 64);
+// 1 + exp(g) rounds to 1.
+__device__ __forceinline__ float silu_times(float g, float u) {
+    if (g >= -80.0f) return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504f)) * u;
+    const float t = exp2f(fmaf(g, 1.44269504088896341f, 64.0f));
+    return ((g * t) * u) * 0x1p-64f;
+}
+
 // Raw buffer resource over [base, base + num_bytes): loads at offsets past the
 // end return zero (gfx9 raw-buffer range check, stride 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {

@@ -57,6 +57,9 @@ struct GemmArgs {
     float acc_bias;           // kAccBias, kept in a scalar register (see biased_acc_to_f32)
     float *partial;           // split K: fp32 partial sums [splits, M, N] (workspace)
     int64_t kb_per_split;     // split K: K blocks per split (the last split may hold fewer)
+    int8_t *aq;               // gated MoE epilogue: int8 codes [M, I] of silu(gate) * up
+    float *as;                // gated MoE epilogue: their scales [M, I / 128]
+    int64_t I;                // gated MoE epilogue: intermediate size (N = 2 I)
 };
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -727,6 +730,19 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 // the last rescale of block kb.  The activation scales reach LDS by
 // buffer-to-LDS loads, eight K blocks at a time, without passing through
 // registers.
+//
+// SILU (grouped form only): the w13 projection with the SiLU gating and the
+// requantisation of its output in the epilogue.  A workgroup owns 128 columns
+// [i0, i0 + 128) of the intermediate activation: weight rows i0.. of the gate
+// half fill tile rows 0-127 (waves wn = 0) and rows I + i0.. of the up half
+// tile rows 128-255 (waves wn = 1), so a gate wave and the up wave of the
+// same wm hold gate and up of the same (token, column) in the same lane and
+// register.  The epilogue rounds both to bf16 (the value the unfused
+// projection stores), passes up through LDS, and the gate waves form
+// bf16(silu(g) * u), the 128-group scale of each token (the group lies in
+// lanes l and l ^ 32) and its int8 codes -- the same operations in the same
+// precision as silu_mul_quant_kernel, so the result is bit-identical to the
+// projection followed by that kernel.  Requires I % 128 == 0.
 struct WideCfg {
     static constexpr int kWaves = 8;
     static constexpr int kThreads = kWaves * 64;
@@ -744,7 +760,7 @@ struct WideCfg {
     static constexpr int kScaleLoads = kBM * kSB / 64 / kWaves;
 };
 
-template <bool MOE>
+template <bool MOE, bool SILU>
 __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = WideCfg;
@@ -753,16 +769,22 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     __shared__ __attribute__((aligned(1024))) char lds1[C::kStageBytes];
     __shared__ float xsl[2][C::kBM * C::kSB];
 
+    static_assert(!SILU || MOE, "the gated epilogue is the grouped w13 projection's");
     Tile t;
-    if (!decode_tile<C::kBN, C::kBM, MOE, kGroupMWide>(p, t)) return;
+    // SILU: t.n0 = i0, the first of the workgroup's 128 intermediate columns
+    if (!decode_tile<SILU ? C::kBN / 2 : C::kBN, C::kBM, MOE, kGroupMWide>(p, t)) return;
     if (t.rows <= 0) return;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t K = p.K, KB = p.KB;
 
-    const int64_t wrows = p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN;
+    // SILU: the load pieces j = 0, 1 (tile rows 0-127) read gate rows i0..
+    // through wr, the pieces j = 2, 3 (tile rows 128-255) up rows I + i0..
+    // through wr_up, at the offsets of pieces j - 2.
+    const int64_t wrows = SILU ? C::kBN / 2 : (p.N - t.n0 < C::kBN ? p.N - t.n0 : C::kBN);
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(t.w + t.n0 * K, clamp_bytes(wrows * K));
+    const __amdgpu_buffer_rsrc_t wr_up = SILU ? make_rsrc(t.w + (p.I + t.n0) * K, clamp_bytes(wrows * K)) : wr;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq + t.m0 * K, clamp_bytes(t.rows * K));
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.xs + t.m0 * KB, clamp_bytes(t.rows * KB * 4));
 
@@ -800,8 +822,10 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024), 16,
-                in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
+                SILU && j >= C::kWLoads / 2 ? wr_up : wr, (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024),
+                16, in_k ? go + kofs + (SILU && j >= C::kWLoads / 2 ? j - C::kWLoads / 2 : j) * piece_stride
+                         : kOobOffset,
+                0, 0, 0);
 #pragma unroll
         for (int j = 0; j < C::kXLoads; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -821,7 +845,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
 #pragma unroll
     for (int b = 0; b < SB; ++b) srow[b] = (wm * C::kWaveM + 32 * b + rr) * C::kSB;
 
-    int64_t nbw = (t.n0 + wn * C::kWaveN) / kBlock;
+    int64_t nbw = (SILU ? t.n0 + wn * p.I : t.n0 + wn * C::kWaveN) / kBlock;
     if (nbw > p.NB - 1) nbw = p.NB - 1;
     const BI8_CONST float *ws_row = reinterpret_cast<const BI8_CONST float *>(
         reinterpret_cast<uintptr_t>(t.ws + nbw * KB));
@@ -932,6 +956,161 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
         if (kb + 2 >= KB) break;
     }
     wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
+
+    if constexpr (SILU) {
+        // Gate wave (wn = 0) and up wave (wn = 1) of one wm share the work:
+        // the gate wave finishes columns a = 0, 1 of its sub-tiles, the up wave
+        // a = 2, 3 (each needs the other's value there), so all four SIMDs
+        // take part.  Values travel as bf16 through LDS: (a, b, register i) of
+        // lane l at slot(b, a) + (i / 8) KB + 16 l + 2 (i % 8).  The group
+        // maximum of a token's 128 columns is then combined over lanes l and
+        // l ^ 32 of both waves.
+        __syncthreads();   // every wave is past its last fragment read: the stages are free
+        char *xbuf = lds0;
+        float *mbuf = &xsl[0][0];   // [wm][wn][b][32] partial group maxima
+        auto slot = [&](int b, int a) { return xbuf + ((wm * SB + b) * SA + a) * 2048 + lane * 16; };
+        auto give = [&](auto a0c) __attribute__((always_inline)) {
+            constexpr int A0 = decltype(a0c)::value;
+#pragma unroll
+            for (int b = 0; b < SB; ++b)
+#pragma unroll
+                for (int a = A0; a < A0 + 2; ++a)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        u32x4 v;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            v[j] = f32x2_to_bf16x2_bits(y[a][b][8 * h + 2 * j], y[a][b][8 * h + 2 * j + 1]);
+                        *reinterpret_cast<u32x4 *>(slot(b, a) + h * 1024) = v;
+                    }
+        };
+        if (wn == 0)
+            give(std::integral_constant<int, 2>{});
+        else
+            give(std::integral_constant<int, 0>{});
+        __syncthreads();
+
+        // a = bf16(silu(g) * u) over the wave's own columns, in place of y;
+        // the per-element SiLU takes its far-negative branch only in a wave
+        // that holds such a gate value (silu_times with g >= -80 is the plain
+        // expression)
+        float amax[SB];
+        auto gate_up = [&](auto a0c, auto gatec) __attribute__((always_inline)) {
+            constexpr int A0 = decltype(a0c)::value;
+            constexpr bool GATE = decltype(gatec)::value;
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                float gv[32], uv[32];
+                float gmin = 0.0f;
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const u32x4 pv = *reinterpret_cast<const u32x4 *>(slot(b, A0 + aa) + h * 1024);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int i = 8 * h + 2 * j, k = 16 * aa + i;
+                            const uint32_t ob = f32x2_to_bf16x2_bits(y[A0 + aa][b][i], y[A0 + aa][b][i + 1]);
+                            const float o0 = bf16_bits_to_f32(ob & 0xFFFFu), o1 = bf16_bits_to_f32(ob >> 16);
+                            const float p0 = bf16_bits_to_f32(pv[j] & 0xFFFFu), p1 = bf16_bits_to_f32(pv[j] >> 16);
+                            gv[k] = GATE ? o0 : p0;
+                            gv[k + 1] = GATE ? o1 : p1;
+                            uv[k] = GATE ? p0 : o0;
+                            uv[k + 1] = GATE ? p1 : o1;
+                            gmin = fminf(gmin, fminf(gv[k], gv[k + 1]));
+                        }
+                    }
+                float am = 0.0f;
+                const bool far = __any(gmin < -80.0f);
+#pragma unroll
+                for (int k = 0; k < 32; k += 2) {
+                    float s0, s1;
+                    if (far) {
+                        s0 = silu_times(gv[k], uv[k]);
+                        s1 = silu_times(gv[k + 1], uv[k + 1]);
+                    } else {
+                        s0 = gv[k] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gv[k] * -1.44269504f)) * uv[k];
+                        s1 = gv[k + 1] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gv[k + 1] * -1.44269504f)) *
+                             uv[k + 1];
+                    }
+                    const uint32_t ab = f32x2_to_bf16x2_bits(s0, s1);
+                    const float a0 = bf16_bits_to_f32(ab & 0xFFFFu), a1 = bf16_bits_to_f32(ab >> 16);
+                    y[A0 + k / 16][b][k % 16] = a0;
+                    y[A0 + k / 16][b][k % 16 + 1] = a1;
+                    am = fmaxf(am, fmaxf(fabsf(a0), fabsf(a1)));
+                }
+                am = fmaxf(am, __shfl_xor(am, 32));
+                amax[b] = am;
+                if (hi == 0) mbuf[((wm * 2 + wn) * SB + b) * 32 + rr] = am;
+            }
+        };
+        if (wn == 0)
+            gate_up(std::integral_constant<int, 0>{}, std::true_type{});
+        else
+            gate_up(std::integral_constant<int, 2>{}, std::false_type{});
+        __syncthreads();
+
+        // codes of the wave's own columns and (gate wave) the group scale;
+        // quant_code's division fallback runs only in a wave that needs it
+        const int64_t I = p.I, IB = I / kBlock, g = t.n0 / kBlock;
+        auto quant_store = [&](auto a0c) __attribute__((always_inline)) {
+            constexpr int A0 = decltype(a0c)::value;
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const float am = fmaxf(amax[b], mbuf[((wm * 2 + (wn ^ 1)) * SB + b) * 32 + rr]);
+                const float sc = am / 127.0f;
+                const float rs = __builtin_amdgcn_rcpf(sc);
+                uint32_t code[2][4];
+                float dmax = 0.0f;
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        uint32_t c = 0u;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = y[A0 + aa][b][4 * i4 + e] * rs;
+                            float q = rintf(v);
+                            dmax = fmaxf(dmax, fabsf(v - q));
+                            q = fminf(fmaxf(q, -127.0f), 127.0f);
+                            c |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * e);
+                        }
+                        code[aa][i4] = c;
+                    }
+                // the products are finite whenever am and rs are; otherwise, or
+                // near a half-integer, take quant_code itself
+                const bool fine = dmax < 0.5f - 0x1p-14f && rs * 0.0f == 0.0f && am * 0.0f == 0.0f;
+                if (__any(sc != 0.0f && !fine)) {
+#pragma unroll
+                    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            uint32_t c = 0u;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                c |= ((uint32_t)quant_code(y[A0 + aa][b][4 * i4 + e], sc, rs) & 0xFFu) << (8 * e);
+                            code[aa][i4] = c;
+                        }
+                }
+                const int64_t ml = wm * C::kWaveM + b * 32 + rr;
+                if (ml >= t.rows) continue;
+                const int64_t r = t.m0 + ml;
+                int8_t *arow = p.aq + r * I + t.n0;
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        *reinterpret_cast<uint32_t *>(arow + (A0 + aa) * 32 + 8 * i4 + 4 * hi) =
+                            sc != 0.0f ? code[aa][i4] : 0u;
+                if (A0 == 0 && hi == 0) p.as[r * IB + g] = sc;
+            }
+        };
+        if (wn == 0)
+            quant_store(std::integral_constant<int, 0>{});
+        else
+            quant_store(std::integral_constant<int, 2>{});
+        return;
+    }
 
 #pragma unroll
     for (int b = 0; b < SB; ++b) {
@@ -1255,9 +1434,10 @@ template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3, false>(Ge
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4, false>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3, true>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4, true>(GemmArgs);
-template __global__ void gemm_wide_kernel<false>(GemmArgs);
+template __global__ void gemm_wide_kernel<false, false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
-template __global__ void gemm_wide_kernel<true>(GemmArgs);
+template __global__ void gemm_wide_kernel<true, false>(GemmArgs);
+template __global__ void gemm_wide_kernel<true, true>(GemmArgs);
 
 // One workgroup per 16 weight rows; 16-token tiles by M.  ODD (K % 16 != 0):
 // the same for every M, in chunks of 64 tokens along the grid's y.
@@ -1318,12 +1498,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
-template <bool MOE>
+template <bool MOE, bool SILU = false>
 hipError_t launch_wide(GemmArgs p, hipStream_t stream) {
     const int64_t total = p.tiles_m * p.tiles_n;
     if (total <= 0) return hipSuccess;
     if (total > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_wide_kernel<MOE>), dim3((unsigned)total), dim3(WideCfg::kThreads), 0,
+    hipLaunchKernelGGL((gemm_wide_kernel<MOE, SILU>), dim3((unsigned)total), dim3(WideCfg::kThreads), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -1516,6 +1696,21 @@ hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, con
         default:
             return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_moe_gemm_silu_quant(const int8_t *xq, const float *xs, const int32_t *offsets, const int8_t *w13,
+                                      const float *ws13, int8_t *aq, float *as, int64_t R, int64_t I, int64_t K,
+                                      int32_t E, hipStream_t stream) {
+    if (I % kBlock != 0) return hipErrorInvalidValue;
+    GemmArgs p = make_args(xq, xs, w13, ws13, nullptr, nullptr, R, 2 * I, K);
+    p.offsets = offsets;
+    p.E = E;
+    p.aq = aq;
+    p.as = as;
+    p.I = I;
+    p.tiles_m = (R + 255) / 256 + E;   // >= sum over experts of ceil(rows_e / 256)
+    p.tiles_n = I / kBlock;
+    return launch_wide<true, true>(p, stream);
 }
 
 }  // namespace bi8

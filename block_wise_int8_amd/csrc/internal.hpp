@@ -64,6 +64,9 @@ hipError_t launch_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
                          uint16_t *y, int64_t M, int64_t N, int64_t K, int32_t block_n, int32_t block_k,
                          int8_t *xq, float *xs, hipStream_t st);
 
+hipError_t launch_moe_gemm_silu_quant(const int8_t *xq, const float *xs, const int32_t *offsets, const int8_t *w13,
+                                      const float *ws13, int8_t *aq, float *as, int64_t R, int64_t I, int64_t K,
+                                      int32_t E, hipStream_t stream);
 hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, const int32_t *offsets,
                            const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
                            int64_t K, int32_t E, hipStream_t stream);

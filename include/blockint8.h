@@ -288,6 +288,9 @@ int32_t blockint8_check_tp_partition(int64_t input_size, int64_t input_size_per_
  *   blockint8_silu_mul_quant     silu(gate) * up -> int8 rows + scales
  *   blockint8_moe_gemm           w2 per expert
  *   blockint8_moe_combine        weighted sum of each token's k rows
+ *
+ * blockint8_moe_gemm_silu_quant does the w13 GEMM and the activation step in
+ * one launch (I % 128 == 0).
  * ------------------------------------------------------------------- */
 
 /*
@@ -347,6 +350,30 @@ int32_t blockint8_quant_act_gather(const uint16_t *x, int64_t T, int64_t ldx, co
  */
 int32_t blockint8_silu_mul_quant(const uint16_t *h, int64_t R, int64_t I, int32_t block_k, int8_t *aq,
                                  float *as, uint16_t *a, void *stream);
+
+/*
+ * The w13 grouped GEMM with the gate/up activation and its quantisation as
+ * the GEMM's epilogue (section 5: per-expert w13 holds the gate and the up
+ * projection; section 6: the runner applies the int8 block arithmetic per
+ * expert and the activation between the two projections).  One launch
+ * computes what blockint8_moe_gemm(xq, xs, expert_offsets, w13, ws13, h,
+ * R, 2I, K, E) followed by blockint8_silu_mul_quant(h, R, I) computes, bit
+ * for bit, without writing h:
+ *
+ *   xq, xs, expert_offsets  as blockint8_moe_gemm (K % 16 == 0)
+ *   w13   int8 [E, 2I, K]: rows [0, I) gate, rows [I, 2I) up
+ *   ws13  fp32 [E, 2I / 128, ceil(K / 128)]
+ *   aq    int8 [R, I]   (output, 16-byte aligned)
+ *   as    fp32 [R, I / 128]   (output)
+ *
+ * Errors: as blockint8_moe_gemm; NULL aq/as (R > 0) -> BI8_ERR_NULL;
+ * I not a positive multiple of 128 -> BI8_ERR_SHAPE; aq not 16-byte or as
+ * not 4-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_moe_gemm_silu_quant(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
+                                      const int8_t *w13, const float *ws13, int8_t *aq, float *as, int64_t R,
+                                      int64_t I, int64_t K, int32_t E, int32_t block_n, int32_t block_k,
+                                      void *stream);
 
 /*
  * Weighted combine: out[t, :] = bf16( sum_s w[t, s] * y2[row_of[t, s], :] ),

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
                           "blockint8_gemm_workspace_size", "blockint8_moe_gemm",
                           "blockint8_linear", "blockint8_linear_noalloc", "blockint8_moe_route", "blockint8_quant_act_gather",
                           "blockint8_quant_weight", "blockint8_check_tp_partition",
-                          "blockint8_silu_mul_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
+                          "blockint8_silu_mul_quant", "blockint8_moe_gemm_silu_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
                           "blockint8_gemm_variant", "blockint8_moe_gemm_variant"}
     for name in names:
         assert hasattr(lib, name), name
@@ -334,6 +334,29 @@ def silu(lib, h=P16, R=4, I=256, bk=128, aq=P16, as_=P16, a=None):
 def test_silu_mul_quant_rejects(lib, kw, status):
     assert silu(lib, **kw) == status
     assert lib.blockint8_last_error().decode().startswith("blockint8_silu_mul_quant")
+
+
+def moe_silu(lib, xq=P16, xs=P16, off=P16, w=P16, ws=P16, aq=P16, as_=P16, R=4, I=256, K=256, E=2, bn=128,
+             bk=128):
+    return lib.blockint8_moe_gemm_silu_quant(xq, xs, off, w, ws, aq, as_, R, I, K, E, bn, bk, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(off=None), NULL), (dict(w=None), NULL), (dict(xq=None), NULL), (dict(aq=None), NULL),
+    (dict(as_=None), NULL),
+    (dict(E=0), SHAPE), (dict(E=65537), SHAPE), (dict(R=-1), SHAPE), (dict(I=0), SHAPE), (dict(I=-128), SHAPE),
+    (dict(I=192), SHAPE), (dict(I=64), SHAPE),   # the fused epilogue takes whole 128-column groups
+    (dict(bn=64), BLOCK), (dict(bk=256), BLOCK),
+    (dict(K=100), ALIGN), (dict(off=P16 + 2), ALIGN), (dict(xq=P16 + 4), ALIGN), (dict(aq=P16 + 4), ALIGN),
+    (dict(as_=P16 + 2), ALIGN), (dict(ws=P16 + 2), ALIGN),
+])
+def test_moe_gemm_silu_quant_rejects(lib, kw, status):
+    assert moe_silu(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_moe_gemm_silu_quant")
+
+
+def test_moe_gemm_silu_quant_empty_is_noop(lib):
+    assert moe_silu(lib, R=0, xq=None, xs=None, off=None, w=None, ws=None, aq=None, as_=None) == OK
 
 
 def combine(lib, y2=P16, R=8, ro=P16, w=P16, T=4, k=2, H=64, out=P16):

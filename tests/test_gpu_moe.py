@@ -129,6 +129,71 @@ def test_combine_stagewise(T, E, k, H):
     assert np.mean(out == ref) >= 0.99
 
 
+FUSED_CASES = [
+    # R, K, I, per-expert row counts (empty experts, ragged tails, several 256-row tiles)
+    (700, 384, 256, [0, 300, 1, 399]),
+    (513, 4096, 1408, [256, 0, 257]),
+    (64, 128, 128, [64]),
+    (1000, 400, 384, [10, 600, 0, 0, 390]),
+]
+
+
+@pytest.mark.parametrize("R,K,I,sizes", FUSED_CASES)
+def test_moe_gemm_silu_quant_is_the_unfused_pipeline(R, K, I, sizes):
+    """The w13 GEMM with the gating epilogue against the two launches it
+    replaces (bit for bit), and that chain against the oracle: h within the
+    GEMM tolerance, a within one bf16 ulp, codes and scales exactly on the
+    GPU's own a.  One expert's gate block gets a large scale (SiLU's far
+    negative branch and large products) and another's last 128 gate and up
+    rows are zero (all-zero groups, scale 0)."""
+    E = len(sizes)
+    assert sum(sizes) == R
+    rng = np.random.default_rng(R + K + I)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    x = wl.activations(rng, R, K)
+    xq, xs = bi8.quant_act(bf16_to_dev(x))
+    w13 = wl.weights(rng, E, 2 * I, K)
+    ws13 = wl.weight_scales(rng, E, *oracle.scale_shape(2 * I, K))
+    ws13[E - 1, 0, :] *= 4096.0                # gate rows 0..127 of the last expert
+    w13[0, I - 128:I] = 0                      # expert 0: last gate group zero
+    w13[0, 2 * I - 128:] = 0                   # and its up rows
+    d_off, d_w, d_ws = to_dev(off), to_dev(w13), to_dev(ws13)
+
+    h = bi8.moe_gemm(xq, xs, d_off, d_w, d_ws)
+    for v in (bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256):
+        assert torch.equal(bi8.moe_gemm(xq, xs, d_off, d_w, d_ws, variant=v).view(torch.int16),
+                           h.view(torch.int16)), "variant %d" % v
+    aq_u, as_u, a_u = bi8.silu_mul_quant(h, return_a=True)
+
+    # outputs inside a larger allocation: the rows past R must stay untouched
+    aq_buf = torch.full((R + 1, I), 0x5A, dtype=torch.int8, device=device())
+    as_buf = torch.full((R + 1, I // 128), -7.0, dtype=torch.float32, device=device())
+    aq, as_ = bi8.moe_gemm_silu_quant(xq, xs, d_off, d_w, d_ws, aq=aq_buf[:R], as_=as_buf[:R])
+    torch.cuda.synchronize()
+    assert torch.equal(aq, aq_u), "codes differ from moe_gemm + silu_mul_quant"
+    assert torch.equal(as_.view(torch.int32), as_u.view(torch.int32)), "scales differ"
+    assert torch.all(aq_buf[R] == 0x5A) and torch.all(as_buf[R] == -7.0)
+    aq2, as2 = bi8.moe_gemm_silu_quant(xq, xs, d_off, d_w, d_ws)   # fresh outputs, same result
+    assert torch.equal(aq2, aq) and torch.equal(as2, as_)
+
+    hb, ab = bf16_bits(h), bf16_bits(a_u)
+    xq_h, xs_h = xq.cpu().numpy(), xs.cpu().numpy()
+    for e in range(E):
+        a0, b0 = int(off[e]), int(off[e + 1])
+        if a0 == b0:
+            continue
+        rows = np.unique(np.concatenate([[a0, b0 - 1], rng.integers(a0, b0, 6)]))
+        ref = oracle.gemm(xq_h[rows], xs_h[rows], w13[e], ws13[e])
+        assert_gemm_close(hb[rows], ref, "h expert %d" % e)
+    assert_bf16_near(ab, oracle.silu_mul(hb), "silu*up", exact_frac=0.995)
+    q_ref, s_ref = oracle.quant_act(ab)
+    assert np.array_equal(aq.cpu().numpy(), q_ref) and np.array_equal(as_.cpu().numpy(), s_ref)
+    z = as_.cpu().numpy()
+    if sizes[0]:
+        assert np.all(z[:sizes[0], -1] == 0.0)   # the zeroed group
+    assert np.all(np.isfinite(z)) and np.all(z[:, :] >= 0)
+
+
 def oracle_moe_layer(x, logits, w13, ws13, w2, ws2, k):
     T, H = x.shape
     E = logits.shape[1]
@@ -197,11 +262,12 @@ def moe_full():
     y2 = bi8.moe_gemm(aq, as_, off, d["w2"], d["ws2"])
     out = bi8.moe_combine(y2, row_of, wts)
     out_layer = bi8.moe_layer(d["x"], d["logits"], d["w13"], d["ws13"], d["w2"], d["ws2"], k)
+    aq_f, as_f = bi8.moe_gemm_silu_quant(xq1, xs1, off, d["w13"], d["ws13"])
     torch.cuda.synchronize()
     host = dict(T=T, H=H, I=I, E=E, k=k, x=x, logits=logits, w13=w13, ws13=ws13, w2=w2, ws2=ws2,
                 ids=ids.cpu().numpy(), wts=wts.cpu().numpy(), st=st.cpu().numpy(), off=off.cpu().numpy(),
                 row_of=row_of.cpu().numpy(), out=bf16_bits(out), out_layer=bf16_bits(out_layer))
-    dev = dict(d, xq1=xq1, xs1=xs1, h=h, aq=aq, as_=as_, a=a, y2=y2, off=off)
+    dev = dict(d, xq1=xq1, xs1=xs1, h=h, aq=aq, as_=as_, a=a, y2=y2, off=off, aq_f=aq_f, as_f=as_f)
     yield host, dev
     del dev, d
     torch.cuda.empty_cache()
@@ -288,6 +354,15 @@ def test_moe_full_size_silu_and_combine_stagewise(moe_full):
     ulp = np.abs(r) * 2.0 ** -7 + 2.0 ** -133
     assert np.all(np.abs(g - r) <= ulp + host["k"] * 2.0 ** -23 * mag), "combine outside the fp32 bound"
     assert np.mean(out == ref) >= 0.99
+
+
+def test_moe_full_size_fused_gating_is_bit_identical(moe_full):
+    """At the full layer size the fused w13 + gating launch writes exactly
+    the codes and scales of the two launches it replaces (which the tests
+    above hold to the oracle stage by stage)."""
+    _, dev = moe_full
+    assert torch.equal(dev["aq_f"], dev["aq"])
+    assert torch.equal(dev["as_f"].view(torch.int32), dev["as_"].view(torch.int32))
 
 
 def test_moe_full_size_layer_end_to_end(moe_full):
