@@ -11,12 +11,11 @@
 //                        largest, picked on the logits (the softmax is
 //                        monotone, so the choice is exact; ties to the lower
 //                        expert), weights exp(l - max) / sum.
-//  * moe_align_kernel    one workgroup: expert histogram, offsets, then a
-//                        stable placement of the rows (t, slot) by (expert,
-//                        t): within an expert the rows keep token order, so
-//                        a row's position is offsets[e] plus the number of
-//                        earlier tokens that chose e (a block-wide ballot
-//                        prefix count per expert and chunk of 1024 tokens).
+//  * moe_align_kernel    one workgroup per expert: a stable placement of the
+//                        rows (t, slot) by (expert, t, slot): a row's
+//                        position is offsets[e] (the pairs routed to lower
+//                        experts) plus the number of earlier (token, slot)
+//                        pairs that chose e (a block-wide scan).
 //  * silu_mul_quant_kernel  a = bf16(silu(gate) * up), then the dynamic
 //                        per-(row, 128-group) quantisation of a, in one pass
 //                        (codes identical to quant_act applied to a).
@@ -31,16 +30,30 @@ namespace {
 constexpr int kAlignThreads = 1024;
 constexpr int kMaxExperts = 1024;
 
+// EMAX > 0 (E <= EMAX): the token's logits are loaded into registers at
+// once, all loads in flight together; EMAX == 0: read from memory as used.
+// Either way the same operations in the same order.
+template <int EMAX>
 __global__ __launch_bounds__(256) void moe_topk_kernel(const float *__restrict__ logits, int64_t T, int32_t E,
                                                        int32_t k, int32_t renorm, int32_t *__restrict__ ids,
                                                        float *__restrict__ weights) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= T) return;
     const float *l = logits + t * E;
+    constexpr int kReg = EMAX > 0 ? EMAX : 1;
+    float lg[kReg];
+    if constexpr (EMAX > 0) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) lg[e] = e < E ? l[e] : -INFINITY;
+    }
+    auto L = [&](int e) __attribute__((always_inline)) { return EMAX > 0 ? lg[e] : l[e]; };
+    constexpr int kLoop = EMAX > 0 ? EMAX : 0x7FFFFFFF;   // e < E is checked as well
     float mx = -INFINITY;
-    for (int e = 0; e < E; ++e) mx = fmaxf(mx, l[e]);
+#pragma unroll
+    for (int e = 0; e < kLoop && e < E; ++e) mx = fmaxf(mx, L(e));
     float sum = 0.0f;
-    for (int e = 0; e < E; ++e) sum += expf(l[e] - mx);
+#pragma unroll
+    for (int e = 0; e < kLoop && e < E; ++e) sum += expf(L(e) - mx);
     // pick k times: the largest logit not yet taken (strict >, so ties go to
     // the lower index); "taken" is kept as the list of chosen ids
     int32_t chosen[8];
@@ -49,12 +62,13 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float *__restrict__
     for (int j = 0; j < k; ++j) {
         int best = -1;
         float bl = 0.0f;
-        for (int e = 0; e < E; ++e) {
+#pragma unroll
+        for (int e = 0; e < kLoop && e < E; ++e) {
             bool taken = false;
             for (int i = 0; i < j; ++i) taken |= chosen[i] == e;
-            if (!taken && (best < 0 || l[e] > bl)) {
+            if (!taken && (best < 0 || L(e) > bl)) {
                 best = e;
-                bl = l[e];
+                bl = L(e);
             }
         }
         chosen[j] = best;
@@ -67,62 +81,130 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float *__restrict__
     }
 }
 
+// One workgroup per expert e.  Rows are ordered by (expert, token, slot), so
+// expert e's rows start at the number of (token, slot) pairs routed to a
+// lower expert, and a row's place among e's rows is the number of pairs
+// routed to e at earlier (token, slot).  Thread i owns Q consecutive tokens
+// of each round of kAlignThreads * Q tokens (their K ids are contiguous):
+// pass 1 counts the pairs below e over all tokens (a block sum), pass 2
+// places e's rows with a block-wide exclusive scan of the per-thread counts.
+// ids outside [0, E) count nowhere and get no row.  The last workgroup also
+// writes offsets[E].
+constexpr int kAlignWaves = kAlignThreads / 64;
+
+// Inclusive prefix sum over the 64 lanes by DPP: shifts right by 1, 2, 4, 8
+// within each row of 16 lanes (lanes shifted in from outside the row add 0),
+// then lane 15 of rows 0 and 2 added to rows 1 and 3, then lane 31 to rows 2
+// and 3.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// Block-wide exclusive prefix (thread order) and total of x.  Two barriers;
+// wsum is reused.
+__device__ __forceinline__ void block_scan(int32_t x, int32_t &before, int32_t &total, int32_t *wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t incl = wave_incl_scan(x);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) {
+        const int32_t c = wsum[w];
+        pre += w < wave ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    before = pre + incl - x;
+    total = tot;
+}
+
+// A round holds at most kAlignThreads * 8 pairs, so the counts of pairs to e
+// (low 16 bits) and below e (high 16 bits) travel packed in one word.
+template <int K>
 __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(const int32_t *__restrict__ ids, int64_t T,
-                                                                  int32_t E, int32_t k,
-                                                                  int32_t *__restrict__ sorted_token,
+                                                                  int32_t E, int32_t *__restrict__ sorted_token,
                                                                   int32_t *__restrict__ offsets,
                                                                   int32_t *__restrict__ row_of) {
-    __shared__ int32_t base[kMaxExperts + 1];
-    __shared__ int32_t wave_tot[kAlignThreads / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e <= E; e += kAlignThreads) base[e] = 0;
-    __syncthreads();
-    // histogram (ids outside [0, E) are not counted and get no row)
-    for (int64_t i = tid; i < T * k; i += kAlignThreads) {
-        const int32_t e = ids[i];
-        if (e >= 0 && e < E) atomicAdd(&base[e], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int32_t run = 0;
-        for (int e = 0; e < E; ++e) {
-            const int32_t c = base[e];
-            base[e] = run;
-            offsets[e] = run;
-            run += c;
+    constexpr int Q = K >= 8 ? 1 : 8 / K;   // tokens per thread and round
+    constexpr int N = Q * K;
+    static_assert(kAlignThreads * N < 65536, "packed counts");
+    __shared__ int32_t wsum[kAlignWaves];
+    const int32_t e = (int32_t)blockIdx.x;
+    const int64_t TK = T * K, round = (int64_t)kAlignThreads * Q;
+    // the thread's N ids of the round from r0 (-1 past the end); every load
+    // is issued (clamped into range) before any is used
+    auto load = [&](int32_t (&v)[N], int64_t r0) __attribute__((always_inline)) {
+        const int64_t i0 = (r0 + (int64_t)threadIdx.x * Q) * K;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int64_t i = i0 + j;
+            const int32_t x = ids[i < TK ? i : TK - 1];
+            v[j] = i < TK ? x : -1;
         }
-        offsets[E] = run;
-    }
-    __syncthreads();
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t c0 = 0; c0 < T; c0 += kAlignThreads) {
-        const int64_t t = c0 + tid;
-        const bool valid = t < T;
-        int32_t my[8];
-        for (int j = 0; j < k; ++j) my[j] = valid ? ids[t * k + j] : -1;
-        for (int e = 0; e < E; ++e) {
-            int slot = -1;
-            for (int j = 0; j < k; ++j)
-                if (my[j] == e) slot = j;
-            const uint64_t m = __ballot(slot >= 0);
-            if (lane == 0) wave_tot[wave] = __popcll(m);
-            __syncthreads();
-            // every thread reads the wave counts now, before the barrier below:
-            // after it the next round overwrites them
-            int32_t pre = 0, tot = 0;
-            for (int w = 0; w < kAlignThreads / 64; ++w) {
-                const int32_t c = wave_tot[w];
-                pre += w < wave ? c : 0;
-                tot += c;
+    };
+    auto counts = [&](const int32_t (&v)[N]) __attribute__((always_inline)) {
+        int32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < N; ++j) c += (v[j] == e ? 1 : 0) + (v[j] >= 0 && v[j] < e ? 0x10000 : 0);
+        return c;
+    };
+    // rows of e among v from row r on, in (token, slot) order
+    auto place = [&](const int32_t (&v)[N], int64_t r0, int32_t r) __attribute__((always_inline)) {
+        const int64_t t0 = r0 + (int64_t)threadIdx.x * Q;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            if (v[j] == e) {
+                const int64_t t = t0 + j / K;
+                sorted_token[r] = (int32_t)t;
+                row_of[t * K + j % K] = r;
+                ++r;
             }
-            if (slot >= 0) {
-                const int32_t pos = base[e] + pre + __popcll(m & below);
-                sorted_token[pos] = (int32_t)t;
-                row_of[t * k + slot] = pos;
-            }
-            __syncthreads();
-            if (tid == 0) base[e] += tot;
         }
+    };
+    auto write_offsets = [&](int32_t below, int32_t mine) __attribute__((always_inline)) {
+        if (threadIdx.x == 0) {
+            offsets[e] = below;
+            if (e == E - 1) offsets[E] = below + mine;
+        }
+    };
+
+    if (T <= round) {   // one round: one load, one scan
+        int32_t v[N];
+        if (T > 0) load(v, 0);
+        else
+#pragma unroll
+            for (int j = 0; j < N; ++j) v[j] = -1;
+        int32_t before, tot;
+        block_scan(counts(v), before, tot, wsum);
+        write_offsets(tot >> 16, tot & 0xFFFF);
+        place(v, 0, (tot >> 16) + (before & 0xFFFF));
+        return;
+    }
+    int32_t below = 0, mine = 0;   // pairs routed below e / to e, over all tokens
+    for (int64_t r0 = 0; r0 < T; r0 += round) {
+        int32_t v[N];
+        load(v, r0);
+        int32_t before, tot;
+        block_scan(counts(v), before, tot, wsum);
+        below += tot >> 16;
+        mine += tot & 0xFFFF;
+    }
+    write_offsets(below, mine);
+    int32_t pos = below;
+    for (int64_t r0 = 0; r0 < T; r0 += round) {
+        int32_t v[N];
+        load(v, r0);
+        int32_t before, tot;
+        block_scan(counts(v) & 0xFFFF, before, tot, wsum);
+        place(v, r0, pos + before);
+        pos += tot;
     }
 }
 
@@ -227,13 +309,33 @@ hipError_t launch_moe_route(const float *logits, int64_t T, int32_t E, int32_t k
     if (T > 0) {
         const int64_t blocks = (T + 255) / 256;
         if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(moe_topk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, logits, T, E, k,
-                           renorm, ids, weights);
+        if (E <= 16)
+            hipLaunchKernelGGL(moe_topk_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, logits, T, E, k,
+                               renorm, ids, weights);
+        else
+            hipLaunchKernelGGL(moe_topk_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, logits, T, E, k,
+                               renorm, ids, weights);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, ids, T, E, k, sorted_token,
-                       offsets, row_of);
+    switch (k) {
+#define BI8_ALIGN_CASE(KK)                                                                                    \
+    case KK:                                                                                                 \
+        hipLaunchKernelGGL(moe_align_kernel<KK>, dim3((unsigned)E), dim3(kAlignThreads), 0, stream, ids, T, E, \
+                           sorted_token, offsets, row_of);                                                   \
+        break;
+        BI8_ALIGN_CASE(1)
+        BI8_ALIGN_CASE(2)
+        BI8_ALIGN_CASE(3)
+        BI8_ALIGN_CASE(4)
+        BI8_ALIGN_CASE(5)
+        BI8_ALIGN_CASE(6)
+        BI8_ALIGN_CASE(7)
+        BI8_ALIGN_CASE(8)
+#undef BI8_ALIGN_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
