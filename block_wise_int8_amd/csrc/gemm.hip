@@ -743,6 +743,10 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 // lanes l and l ^ 32) and its int8 codes -- the same operations in the same
 // precision as silu_mul_quant_kernel, so the result is bit-identical to the
 // projection followed by that kernel.  Requires I % 128 == 0.
+#ifndef BI8_WIDE_SPREAD_FILLS
+#define BI8_WIDE_SPREAD_FILLS 1
+#endif
+constexpr bool kSpreadFills = BI8_WIDE_SPREAD_FILLS;
 struct WideCfg {
     static constexpr int kWaves = 8;
     static constexpr int kThreads = kWaves * 64;
@@ -806,9 +810,13 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // K blocks this lane's 16-byte chunk lies in: kb < kb_in <=> kb * 128 + chunk < K
     const int kb_in = (int)((K - chunk + kBlock - 1) / kBlock);
 
-    auto issue = [&](char *stage, int64_t kb) __attribute__((always_inline)) {
+    // part p < 0: every load of block kb; part p >= 0: weight piece p and
+    // activation piece p (and with p == 0 the scale batch), so that a block's
+    // fills can be spread over its first sub-tiles instead of queueing in
+    // the address unit all at once.
+    auto issue = [&](char *stage, int64_t kb, int part) __attribute__((always_inline)) {
         const uint32_t kofs = (uint32_t)kb * kBlock;
-        if ((kb & (C::kSB - 1)) == 0) {
+        if (part <= 0 && (kb & (C::kSB - 1)) == 0) {
             // The batch of activation scales goes straight to LDS, 4 bytes a
             // lane.  Entries past the last K block read the next row's scales
             // (or zero past the end of xs): they are never used, so no check.
@@ -818,19 +826,22 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
                     sr, (BI8_LDS void *)&xsl[(kb / C::kSB) & 1][(wave * C::kScaleLoads + j) * 64], 4,
                     sofs[j] + (uint32_t)kb * 4u, 0, 0, 0);
         }
+        // Only the activation chunks past K are zeroed: the weight bytes there
+        // (the next row's, or zero past the buffer) multiply zeros.
         const bool in_k = (int)kb < kb_in;
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                SILU && j >= C::kWLoads / 2 ? wr_up : wr, (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024),
-                16, in_k ? go + kofs + (SILU && j >= C::kWLoads / 2 ? j - C::kWLoads / 2 : j) * piece_stride
-                         : kOobOffset,
-                0, 0, 0);
+            if (part < 0 || part == j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    SILU && j >= C::kWLoads / 2 ? wr_up : wr,
+                    (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024), 16,
+                    go + kofs + (SILU && j >= C::kWLoads / 2 ? j - C::kWLoads / 2 : j) * piece_stride, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < C::kXLoads; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
-                in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
+            if (part < 0 || part == j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
+                    in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
     };
 
     const int wn = wave % C::WN, wm = wave / C::WN;
@@ -912,7 +923,10 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // sub-tile's MFMAs, and the last one after the next block's first
     // fragment reads.
     auto compute = [&](const char *stage, char *nxt, int64_t kb) __attribute__((always_inline)) {
-        issue(nxt, kb + 1);
+        // past the last block nothing is loaded (the stage it would fill is
+        // never read)
+        const bool more = kb + 1 < KB;
+        if (!kSpreadFills && more) issue(nxt, kb + 1, -1);
         float tb[SB];
 #pragma unroll
         for (int b = 0; b < SB; ++b) tb[b] = xsv[b] * wsv;
@@ -931,6 +945,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
                 for (int s = 0; s < 4; ++s)
                     acc[j & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[s], xf[b][s],
                                                                          s == 0 ? zero16 : acc[j & 1], 0, 0, 0);
+                if (kSpreadFills && j < C::kWLoads && more) issue(nxt, kb + 1, j);
                 if (j > 0) {
                     const int pa = (j - 1) / SB, pb = (j - 1) % SB;
                     rescale(acc[(j - 1) & 1], y[pa][pb], tb[pb]);
@@ -944,7 +959,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
         rescale(acc[(SA * SB - 1) & 1], y[SA - 1][SB - 1], tb[SB - 1]);
     };
 
-    issue(lds0, 0);
+    issue(lds0, 0, -1);
     wait_vmcnt<0>();
     lds_barrier();
     read_first(lds0, 0);
