@@ -810,13 +810,13 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // K blocks this lane's 16-byte chunk lies in: kb < kb_in <=> kb * 128 + chunk < K
     const int kb_in = (int)((K - chunk + kBlock - 1) / kBlock);
 
-    // part p < 0: every load of block kb; part p >= 0: weight piece p and
-    // activation piece p (and with p == 0 the scale batch), so that a block's
-    // fills can be spread over its first sub-tiles instead of queueing in
-    // the address unit all at once.
-    auto issue = [&](char *stage, int64_t kb, int part) __attribute__((always_inline)) {
+    // The loads of block kb named by `mask`: bit j weight piece j, bit 4 + j
+    // activation piece j, bit 8 the scale batch (when kb starts one).  A
+    // block's fills are spread over its sub-tiles instead of queueing in the
+    // address unit all at once.
+    auto issue = [&](char *stage, int64_t kb, unsigned mask) __attribute__((always_inline)) {
         const uint32_t kofs = (uint32_t)kb * kBlock;
-        if (part <= 0 && (kb & (C::kSB - 1)) == 0) {
+        if ((mask & 0x100u) && (kb & (C::kSB - 1)) == 0) {
             // The batch of activation scales goes straight to LDS, 4 bytes a
             // lane.  Entries past the last K block read the next row's scales
             // (or zero past the end of xs): they are never used, so no check.
@@ -831,14 +831,14 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
         const bool in_k = (int)kb < kb_in;
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
-            if (part < 0 || part == j)
+            if (mask & (1u << j))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     SILU && j >= C::kWLoads / 2 ? wr_up : wr,
                     (BI8_LDS void *)(stage + (wave + j * C::kWaves) * 1024), 16,
                     go + kofs + (SILU && j >= C::kWLoads / 2 ? j - C::kWLoads / 2 : j) * piece_stride, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < C::kXLoads; ++j)
-            if (part < 0 || part == j)
+            if (mask & (1u << (4 + j)))
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
                     in_k ? go + kofs + j * piece_stride : kOobOffset, 0, 0, 0);
@@ -851,10 +851,21 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
 #pragma unroll
     for (int s = 0; s < 4; ++s) frag_off[s] = 16 * ((2 * s + hi) ^ swz);
     const int wrow0 = (wn * C::kWaveN + rr) * 128;
-    const int xrow0 = C::kXOff + (wm * C::kWaveM + rr) * 128;
+    // Sub-tile row block b of wave wm holds tile rows b * 128 + wm * 32 + [0, 32):
+    // a tile of at most 128 rows (the last of an expert's segment, say) keeps
+    // every wave's rows in b = 0, and a wave whose row blocks lie past the
+    // tile's rows skips their MFMAs, fragment reads and rescales (ACT below).
+    auto trow = [&](int b) { return b * (C::kBM / SB) + wm * 32 + rr; };
+    const int xrow0 = C::kXOff + (wm * 32 + rr) * 128;
     int srow[SB];
 #pragma unroll
-    for (int b = 0; b < SB; ++b) srow[b] = (wm * C::kWaveM + 32 * b + rr) * C::kSB;
+    for (int b = 0; b < SB; ++b) srow[b] = trow(b) * C::kSB;
+    // row blocks of this wave holding a row of the tile (a block past the
+    // rows implies every later one is)
+    int act = 0;
+#pragma unroll
+    for (int b = 0; b < SB; ++b) act += b * (C::kBM / SB) + wm * 32 < t.rows;
+    act = __builtin_amdgcn_readfirstlane(act);
 
     int64_t nbw = (SILU ? t.n0 + wn * p.I : t.n0 + wn * C::kWaveN) / kBlock;
     if (nbw > p.NB - 1) nbw = p.NB - 1;
@@ -893,16 +904,20 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // registers they reuse.
     i32x4 xf[SB][4], wf0[4];
     float xsv[SB], wsv;
-    auto read_first = [&](const char *stage, int64_t kb) __attribute__((always_inline)) {
+    // ACT: the wave's active row blocks (b < ACT)
+    auto read_first = [&](auto actc, const char *stage, int64_t kb) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(actc)::value;
 #pragma unroll
-        for (int b = 0; b < SB; ++b) xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
+        for (int b = 0; b < ACT; ++b) xsv[b] = xsl[(kb / C::kSB) & 1][srow[b] + (kb & (C::kSB - 1))];
+        if constexpr (ACT > 0) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) wf0[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + frag_off[s]);
+            for (int s = 0; s < 4; ++s) wf0[s] = *reinterpret_cast<const i32x4 *>(stage + wrow0 + frag_off[s]);
+        }
 #pragma unroll
-        for (int b = 0; b < SB; ++b)
+        for (int b = 0; b < ACT; ++b)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * 32 * 128 + frag_off[s]);
+                xf[b][s] = *reinterpret_cast<const i32x4 *>(stage + xrow0 + b * (C::kBM / SB) * 128 + frag_off[s]);
         wsv = ws_cur;
         ws_cur = ws_row[kb + 1 < KB ? kb + 1 : KB - 1];   // next block's, issued a block ahead
     };
@@ -910,10 +925,10 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // is past the barrier (which also ends every read of block kb): read its
     // first fragments from `nxt`.  After the last block this reads stale LDS
     // that nothing uses.
-    auto advance = [&](const char *nxt, int64_t kb) __attribute__((always_inline)) {
+    auto advance = [&](auto actc, const char *nxt, int64_t kb) __attribute__((always_inline)) {
         wait_vmcnt<0>();
         lds_barrier();
-        read_first(nxt, kb + 1);
+        read_first(actc, nxt, kb + 1);
     };
 
     // One K block: first the fills of block kb + 1 into the other stage (its
@@ -922,14 +937,19 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
     // (0,1), (1,0), ...; the rescale of each sub-tile is issued after the next
     // sub-tile's MFMAs, and the last one after the next block's first
     // fragment reads.
-    auto compute = [&](const char *stage, char *nxt, int64_t kb) __attribute__((always_inline)) {
+    auto compute = [&](auto actc, const char *stage, char *nxt, int64_t kb) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(actc)::value;
         // past the last block nothing is loaded (the stage it would fill is
         // never read)
         const bool more = kb + 1 < KB;
-        if (!kSpreadFills && more) issue(nxt, kb + 1, -1);
+        if ((!kSpreadFills || ACT == 0) && more) issue(nxt, kb + 1, 0x1FFu);
+        if constexpr (ACT == 0) {
+            advance(actc, nxt, kb);
+            return;
+        }
         float tb[SB];
 #pragma unroll
-        for (int b = 0; b < SB; ++b) tb[b] = xsv[b] * wsv;
+        for (int b = 0; b < ACT; ++b) tb[b] = xsv[b] * wsv;
         i32x16 acc[2];
 #pragma unroll
         for (int a = 0; a < SA; ++a) {
@@ -939,36 +959,53 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
                 wf[s] = a == 0 ? wf0[s]
                                : *reinterpret_cast<const i32x4 *>(stage + wrow0 + a * 32 * 128 + frag_off[s]);
 #pragma unroll
-            for (int b = 0; b < SB; ++b) {
-                const int j = a * SB + b;
+            for (int b = 0; b < ACT; ++b) {
+                const int j = a * ACT + b;
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     acc[j & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[s], xf[b][s],
                                                                          s == 0 ? zero16 : acc[j & 1], 0, 0, 0);
-                if (kSpreadFills && j < C::kWLoads && more) issue(nxt, kb + 1, j);
+                // weight and activation piece j after sub-tile j's MFMAs (j < 4;
+                // spread over all eight sub-tiles the last fills came late)
+                if (kSpreadFills && j < 4 && more) issue(nxt, kb + 1, (0x11u << j) | (j == 0 ? 0x100u : 0u));
                 if (j > 0) {
-                    const int pa = (j - 1) / SB, pb = (j - 1) % SB;
+                    const int pa = (j - 1) / ACT, pb = (j - 1) % ACT;
                     rescale(acc[(j - 1) & 1], y[pa][pb], tb[pb]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         // the last sub-tile's MFMAs stay ahead of the barrier as well
-        asm volatile("" ::"v"(acc[(SA * SB - 1) & 1]));
-        advance(nxt, kb);
-        rescale(acc[(SA * SB - 1) & 1], y[SA - 1][SB - 1], tb[SB - 1]);
+        asm volatile("" ::"v"(acc[(SA * ACT - 1) & 1]));
+        advance(actc, nxt, kb);
+        rescale(acc[(SA * ACT - 1) & 1], y[SA - 1][ACT - 1], tb[ACT - 1]);
     };
 
-    issue(lds0, 0, -1);
-    wait_vmcnt<0>();
-    lds_barrier();
-    read_first(lds0, 0);
-    for (int64_t kb = 0;; kb += 2) {
-        // block kb in lds0, block kb + 1 in lds1
-        compute(lds0, lds1, kb);
-        if (kb + 1 >= KB) break;
-        compute(lds1, lds0, kb + 1);
-        if (kb + 2 >= KB) break;
+    auto run = [&](auto actc) __attribute__((always_inline)) {
+        issue(lds0, 0, 0x1FFu);
+        wait_vmcnt<0>();
+        lds_barrier();
+        read_first(actc, lds0, 0);
+        for (int64_t kb = 0;; kb += 2) {
+            // block kb in lds0, block kb + 1 in lds1
+            compute(actc, lds0, lds1, kb);
+            if (kb + 1 >= KB) break;
+            compute(actc, lds1, lds0, kb + 1);
+            if (kb + 2 >= KB) break;
+        }
+    };
+    // (a wave with no row of the tile takes the one-block variant: its
+    // block reads zeros).  Only the gated kernel takes two variants: in the
+    // others the allocation of the pair spills in the full variant's loop,
+    // and the reload waits behind the outstanding fills.
+    static_assert(SB == 2, "row-block variants");
+    if constexpr (SILU) {
+        if (act == SB)
+            run(std::integral_constant<int, SB>{});
+        else
+            run(std::integral_constant<int, 1>{});
+    } else {
+        run(std::integral_constant<int, SB>{});
     }
     wait_vmcnt<0>();   // no LDS fill may outlive the workgroup
 
@@ -1107,7 +1144,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
                             code[aa][i4] = c;
                         }
                 }
-                const int64_t ml = wm * C::kWaveM + b * 32 + rr;
+                const int64_t ml = trow(b);
                 if (ml >= t.rows) continue;
                 const int64_t r = t.m0 + ml;
                 int8_t *arow = p.aq + r * I + t.n0;
@@ -1129,7 +1166,7 @@ __global__ __launch_bounds__(WideCfg::kThreads) void gemm_wide_kernel(GemmArgs p
 
 #pragma unroll
     for (int b = 0; b < SB; ++b) {
-        const int64_t ml = wm * C::kWaveM + b * 32 + rr;
+        const int64_t ml = trow(b);
         if (ml >= t.rows) continue;
         uint16_t *yrow = p.y + (t.m0 + ml) * p.N;
 #pragma unroll
