@@ -338,6 +338,10 @@ constexpr int64_t kSplitKTarget = BI8_SPLITK_TARGET;
 constexpr int64_t kSplitKMaxOutputs = 640 * 1024;
 constexpr int kSplitKStages = BI8_SPLITK_STAGES;
 constexpr int64_t kGroupMWide = 4;
+#ifndef BI8_TILED_SPREAD_FILLS
+#define BI8_TILED_SPREAD_FILLS 1
+#endif
+constexpr bool kSpreadTiled = BI8_TILED_SPREAD_FILLS;
 
 struct Tile {
     int64_t n0;    // first weight row / output column
@@ -470,10 +474,14 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     // are loaded into registers (issued first, so they complete with the
     // stage); they are written to LDS one step before the batch is used.
     // (lb: the block's index within this workgroup's run; kb0 + lb: in K)
-    auto issue = [&](char *stage, int64_t lb) __attribute__((always_inline)) {
+    // part: -1 every load of the stage; 0 / 1 the scales and the first half
+    // of the pieces / the second half (ping-pong spreads a stage's loads over
+    // the two halves of a step)
+    auto issue = [&](char *stage, int64_t lb, const int part = -1) __attribute__((always_inline)) {
         const int64_t k0 = (kb0 + lb) * kBlock;
         const uint32_t kofs = (uint32_t)k0;
-        if ((lb & (C::kSB - 1)) == 0) {
+        auto mine = [&](int j, int n) { return part < 0 || (part == 0) == (j < (n + 1) / 2); };
+        if (part <= 0 && (lb & (C::kSB - 1)) == 0) {
 #pragma unroll
             for (int j = 0; j < C::kScaleLoads; ++j) {
                 const int f = (wave * C::kScaleLoads + j) * 64 + lane;
@@ -483,14 +491,16 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int j = 0; j < C::kWLoads; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (BI8_LDS void *)(stage + C::kWOff + (wave + j * C::kWaves) * 1024), 16,
-                (k0 + wchunk[j] < kend) ? wgo[j] + kofs : kOobOffset, 0, 0, 0);
+            if (mine(j, C::kWLoads))
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, (BI8_LDS void *)(stage + C::kWOff + (wave + j * C::kWaves) * 1024), 16,
+                    (k0 + wchunk[j] < kend) ? wgo[j] + kofs : kOobOffset, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < C::kXLoads; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
-                (k0 + xchunk[j] < kend) ? xgo[j] + kofs : kOobOffset, 0, 0, 0);
+            if (mine(j, C::kXLoads))
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (BI8_LDS void *)(stage + C::kXOff + (wave + j * C::kWaves) * 1024), 16,
+                    (k0 + xchunk[j] < kend) ? xgo[j] + kofs : kOobOffset, 0, 0, 0);
     };
     // Write the scale batch held in registers to LDS buffer `half`, and make it
     // visible before the next barrier.
@@ -609,17 +619,19 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
                     __attribute__((always_inline)) {
         wait_stage(kb);
         lds_barrier();
-        issue(ahead, kb + NS - 1);
+        issue(ahead, kb + NS - 1, kSpreadTiled && PING ? 0 : -1);
         if (!PING) {
             mma(cur, kb, buf);
             if (kb > 0) epi(buf ^ 1);   // block kb - 1, under block kb's MFMAs
         } else if (group == 0) {
             mma(cur, kb, 0);
             lds_barrier();
+            if (kSpreadTiled) issue(ahead, kb + NS - 1, 1);
             epi(0);
         } else {
             if (kb > 0) epi(0);   // block kb - 1
             lds_barrier();
+            if (kSpreadTiled) issue(ahead, kb + NS - 1, 1);
             mma(cur, kb, 0);
         }
         // the next block opens a new scale batch: publish it (its loads were
