@@ -7,7 +7,8 @@ A step is one pass of the hot path over one batch of synthetic input already
 resident in HBM.  The default workload is the block-INT8 FusedMoE layer, the
 largest of the measured configurations (4096 tokens, hidden 4096,
 intermediate 14336, top-2 of 8 experts, [128,128] blocks): route, gather +
-quantise, w13 grouped GEMM, SiLU gating + requantise, w2 grouped GEMM,
+quantise, w13 grouped GEMM with the SiLU gating and requantisation as its
+epilogue (two launches when a kernel variant is forced), w2 grouped GEMM,
 combine.  The dense workloads (``--workload decode|prefill|...``) step
 through dynamic activation quantisation (bf16 -> int8 + fp32 scales)
 followed by the block-scaled int8 GEMM.
