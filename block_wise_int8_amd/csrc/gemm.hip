@@ -1643,12 +1643,15 @@ GemmPath select_gemm_path(int64_t M, int64_t N, int64_t K) {
 }
 
 // Grouped GEMM: the expert segments are ragged, so the tile count is taken
-// from the mean segment length.
+// from the mean segment length.  The 256 x 256 kernel needs four full rounds
+// of the chip's CUs: with fewer its coarse tiles leave a large last round, and
+// the 256 x 128 ping-pong kernel is faster (measured: the MoE w2 projection,
+// 544 wide tiles, 707 -> 650 us; w13, 3808 wide tiles, the two within 1 %).
 GemmPath select_moe_gemm_path(int64_t R, int64_t N, int64_t K, int32_t E) {
     (void)K;
     const int64_t rows_per_expert = E > 0 ? R / E : R;
     const int64_t wide_tiles = (int64_t)E * ((rows_per_expert + 255) / 256) * ((N + 255) / 256);
-    return wide_tiles >= 512 ? GemmPath::kTile256x256 : GemmPath::kTile256x128;
+    return wide_tiles >= 1024 ? GemmPath::kTile256x256 : GemmPath::kTile256x128;
 }
 
 hipError_t launch_gemm(GemmPath path, const int8_t *xq, const float *xs, const int8_t *w,

@@ -201,7 +201,8 @@ def test_gemm_select(lib, M, N, K, variant):
 
 def test_moe_gemm_select(lib):
     assert bi8.moe_gemm_select(8192, 28672, 4096, 8) == bi8.GEMM_TILE_256X256
-    assert bi8.moe_gemm_select(8192, 4096, 14336, 8) == bi8.GEMM_TILE_256X256
+    assert bi8.moe_gemm_select(8192, 4096, 14336, 8) == bi8.GEMM_TILE_256X128   # 512 wide tiles: 2 rounds
+    assert bi8.moe_gemm_select(16384, 4096, 14336, 8) == bi8.GEMM_TILE_256X256  # 1024: 4 rounds
     assert bi8.moe_gemm_select(512, 4096, 4096, 8) == bi8.GEMM_TILE_256X128
 
 
