@@ -135,6 +135,9 @@ FUSED_CASES = [
     (513, 4096, 1408, [256, 0, 257]),
     (64, 128, 128, [64]),
     (1000, 400, 384, [10, 600, 0, 0, 390]),
+    (1, 16, 128, [0, 1, 0]),            # one row, K of one partial block
+    (300, 144, 256, [300]),             # one expert, a ragged second K block
+    (129, 2048, 128, [128, 1]),         # a 128-row tile and a 1-row tile
 ]
 
 
