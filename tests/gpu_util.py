@@ -65,7 +65,7 @@ def assert_gemm_close(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = ""):
 
 
 def host_threads() -> int:
-    """CPU threads this process may use (at most 16: the GPU machine's share)."""
+    """CPU threads this process may use, at most 16."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
