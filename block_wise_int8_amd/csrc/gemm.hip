@@ -353,12 +353,36 @@ struct Tile {
 
 template <int BN, int BM, bool MOE, int64_t GM = kGroupM>
 __device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
-    const int64_t total = p.tiles_m * p.tiles_n;
-    const int64_t tid = xcd_remap(blockIdx.x, total);
+    // MoE: the grid holds an upper bound of m-tiles (the segments' lengths are
+    // only known on the device); the tiles that exist are counted here and
+    // spread evenly over the XCDs, and the surplus workgroups exit.  (Mapped
+    // over the whole grid instead, the missing tiles -- all at the end of the
+    // order -- left the last XCD nearly idle: at R = 8192 over 8 experts the
+    // w13 grid gave six XCDs 560 tiles each and one XCD 56.)
+    int64_t tiles_m = p.tiles_m;
+    if constexpr (MOE) {
+        tiles_m = 0;
+        for (int32_t e = 0; e < p.E; ++e) {
+            int64_t a = p.offsets[e], b = p.offsets[e + 1];
+            a = a < 0 ? 0 : (a > p.M ? p.M : a);
+            b = b < a ? a : (b > p.M ? p.M : b);
+            tiles_m += (b - a + BM - 1) / BM;
+        }
+    }
+    const int64_t total = tiles_m * p.tiles_n;
+    int64_t tid;
+    if constexpr (MOE) {
+        const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int64_t q = total >> 3, r = total & 7;
+        if (slot >= q + (xcd < r ? 1 : 0)) return false;
+        tid = xcd * q + (xcd < r ? xcd : r) + slot;
+    } else {
+        tid = xcd_remap(blockIdx.x, total);
+    }
     // grouped order: GM m-tiles advance together along n
     const int64_t group = tid / (GM * p.tiles_n);
     const int64_t first_m = group * GM;
-    const int64_t gsize = p.tiles_m - first_m < GM ? p.tiles_m - first_m : GM;
+    const int64_t gsize = tiles_m - first_m < GM ? tiles_m - first_m : GM;
     const int64_t in = tid - group * GM * p.tiles_n;
     int64_t tm = first_m + in % gsize;
     const int64_t tn = in / gsize;
