@@ -221,6 +221,10 @@ class Moe:
         self.xs2 = torch.empty((self.R, KB2), dtype=torch.float32, **d)
         self.y2 = torch.empty((self.R, H), dtype=torch.bfloat16, **d)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, **d)
+        # w2's workspace (the tiles of a partial last round split over K), as
+        # the layer allocates it
+        nb = bi8.moe_gemm_workspace_size(self.R, H, I, E) if variant is None else 0
+        self.wsp2 = torch.empty(nb, dtype=torch.uint8, **d) if nb else None
         self.copies = 1
         self.quant_shape = (self.R, H)   # the gathered rows
         self.ops = 2 * self.R * (2 * I) * H + 2 * self.R * H * I
@@ -242,6 +246,10 @@ class Moe:
     def quant(self, i):
         bi8.quant_act_gather(self.x, self.st, self.xq1, self.xs1)
 
+    def launch_w2(self, i):
+        bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2, variant=self.variant,
+                     workspace=self.wsp2)
+
     def launch_w13(self, i):
         bi8.moe_gemm(self.xq1, self.xs1, self.off, self.w13, self.ws13, y=self.y13, variant=self.variant)
 
@@ -262,7 +270,7 @@ class Moe:
         else:
             self.launch_w13(i)
             bi8.silu_mul_quant(self.y13, self.xq2, self.xs2)
-        bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2, variant=self.variant)
+        self.launch_w2(i)
         bi8.moe_combine(self.y2, self.row_of, self.wts, out=self.out)
 
     def parts(self):
@@ -276,9 +284,7 @@ class Moe:
             "moe_gemm_w13": (self.launch_w13, self.w13_bytes),
             "silu_mul_quant": (lambda i: bi8.silu_mul_quant(self.y13, self.xq2, self.xs2),
                                2 * R * 2 * I + R * I + 4 * R * KB2),
-            "moe_gemm_w2": (lambda i: bi8.moe_gemm(self.xq2, self.xs2, self.off, self.w2, self.ws2, y=self.y2,
-                                                   variant=self.variant),
-                            R * I + 4 * R * KB2 + self.E * H * I + 2 * R * H),
+            "moe_gemm_w2": (self.launch_w2, R * I + 4 * R * KB2 + self.E * H * I + 2 * R * H),
             "combine": (lambda i: bi8.moe_combine(self.y2, self.row_of, self.wts, out=self.out),
                         2 * R * H + 8 * T * k + 2 * T * H),
         }

@@ -28,7 +28,7 @@ import os
 import torch
 
 __all__ = ["BlockInt8Error", "lib_path", "load", "scale_shape", "quant_act", "gemm", "gemm_ws",
-           "gemm_workspace_size", "moe_gemm",
+           "gemm_workspace_size", "moe_gemm", "moe_gemm_workspace_size",
            "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES", "gemm_select", "moe_gemm_select", "moe_route", "quant_act_gather",
            "silu_mul_quant", "moe_gemm_silu_quant", "moe_combine", "moe_layer", "quant_weight", "check_tp_partition", "BLOCK", "GEMM_AUTO", "GEMM_SKINNY",
            "GEMM_TILE_128X64", "GEMM_TILE_256X128", "GEMM_TILE_256X256"]
@@ -84,6 +84,9 @@ def load() -> ctypes.CDLL:
     lib.blockint8_moe_gemm_select.argtypes = [i64, i64, i64, i32]
     lib.blockint8_gemm_variant.argtypes = [i32] + lib.blockint8_gemm.argtypes
     lib.blockint8_moe_gemm_variant.argtypes = [i32] + lib.blockint8_moe_gemm.argtypes
+    lib.blockint8_moe_gemm_ws.argtypes = lib.blockint8_moe_gemm.argtypes[:-1] + [vp, i64, vp]
+    lib.blockint8_moe_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.blockint8_moe_gemm_workspace_size.restype = i64
     lib.blockint8_linear.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
     lib.blockint8_linear_noalloc.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     lib.blockint8_moe_route.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -98,7 +101,8 @@ def load() -> ctypes.CDLL:
               "blockint8_moe_route", "blockint8_quant_act_gather", "blockint8_quant_weight",
               "blockint8_check_tp_partition", "blockint8_silu_mul_quant", "blockint8_moe_gemm_silu_quant",
               "blockint8_moe_combine", "blockint8_gemm_select",
-              "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant"):
+              "blockint8_moe_gemm_select", "blockint8_gemm_variant", "blockint8_moe_gemm_variant",
+              "blockint8_moe_gemm_ws"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -253,12 +257,15 @@ def gemm_ws(xq: torch.Tensor, xs: torch.Tensor, w: torch.Tensor, ws: torch.Tenso
 
 def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w: torch.Tensor,
              ws: torch.Tensor, y: torch.Tensor | None = None, block=(BLOCK, BLOCK),
-             variant: int | None = None) -> torch.Tensor:
+             variant: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Grouped block-scaled int8 GEMM over expert-sorted rows -> bf16 [R, N].
 
     ``expert_offsets`` is int32 [E+1] on the device (rows [off[e], off[e+1])
     use expert e); ``w`` is int8 [E, N, K], ``ws`` fp32 [E, ceil(N/128), ceil(K/128)].
     ``variant`` runs a named kernel (``GEMM_TILE_256X128`` or ``GEMM_TILE_256X256``).
+    ``workspace`` (a contiguous device tensor of at least
+    ``moe_gemm_workspace_size`` bytes; not with ``variant``) lets the tiles of
+    a partial last round run split over K (``blockint8_moe_gemm_ws``).
     """
     _need(xq, "xq", torch.int8, 2)
     _need(xs, "xs", torch.float32, 2)
@@ -280,12 +287,25 @@ def moe_gemm(xq: torch.Tensor, xs: torch.Tensor, expert_offsets: torch.Tensor, w
     if tuple(y.shape) != (R, N):
         raise ValueError("y must be [R, N]")
     args = (_ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(w), _ptr(ws), _ptr(y), R, N, K, E,
-            block[0], block[1], _stream_handle(xq.device))
-    if variant is None:
-        _check(load().blockint8_moe_gemm(*args))
+            block[0], block[1])
+    if workspace is not None:
+        if variant is not None:
+            raise ValueError("a workspace runs the default kernel choice (no variant)")
+        if (not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda"
+                or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous tensor on a HIP device")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(load().blockint8_moe_gemm_ws(*args, _ptr(workspace), nbytes, _stream_handle(xq.device)))
+    elif variant is None:
+        _check(load().blockint8_moe_gemm(*args, _stream_handle(xq.device)))
     else:
-        _check(load().blockint8_moe_gemm_variant(int(variant), *args))
+        _check(load().blockint8_moe_gemm_variant(int(variant), *args, _stream_handle(xq.device)))
     return y
+
+
+def moe_gemm_workspace_size(R: int, N: int, K: int, E: int, block=(BLOCK, BLOCK)) -> int:
+    """Bytes of workspace ``moe_gemm`` can use for the grouped problem (0: none)."""
+    return int(load().blockint8_moe_gemm_workspace_size(R, N, K, E, block[0], block[1]))
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, ws: torch.Tensor, bias: torch.Tensor | None = None,
@@ -515,7 +535,11 @@ def moe_layer(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, ws13: to
     else:
         h = moe_gemm(xq, xs, off, w13, ws13, variant=variant)
         aq, as_ = silu_mul_quant(h)
-    y2 = moe_gemm(aq, as_, off, w2, ws2, variant=variant)
+    wsp = None
+    if variant is None:
+        nbytes = moe_gemm_workspace_size(aq.shape[0], w2.shape[1], aq.shape[1], w2.shape[0])
+        wsp = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    y2 = moe_gemm(aq, as_, off, w2, ws2, variant=variant, workspace=wsp)
     return moe_combine(y2, row_of, w)
 
 

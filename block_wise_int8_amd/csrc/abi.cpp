@@ -295,6 +295,34 @@ int32_t blockint8_moe_gemm_variant(int32_t variant, const int8_t *xq, const floa
                                                static_cast<hipStream_t>(stream)));
 }
 
+int64_t blockint8_moe_gemm_workspace_size(int64_t R, int64_t N, int64_t K, int32_t E, int32_t block_n,
+                                          int32_t block_k) {
+    if (R <= 0 || R > kMaxRows || N <= 0 || N > kMaxRows || K <= 0 || K % 16 != 0 || E <= 0 || E > 65536 ||
+        block_n != 128 || block_k != 128)
+        return 0;
+    return bi8::moe_gemm_workspace_bytes(R, N, K, E);
+}
+
+int32_t blockint8_moe_gemm_ws(const int8_t *xq, const float *xs, const int32_t *expert_offsets, const int8_t *w,
+                              const float *ws, uint16_t *y, int64_t R, int64_t N, int64_t K, int32_t E,
+                              int32_t block_n, int32_t block_k, void *workspace, int64_t workspace_bytes,
+                              void *stream) {
+    static const char fn[] = "blockint8_moe_gemm_ws";
+    if (E <= 0 || E > 65536) return fail(BI8_ERR_SHAPE, "%s: E = %d out of range [1, 65536]", fn, E);
+    int32_t s = check_gemm_common(fn, xq, xs, w, ws, y, R, N, K, block_n, block_k, false, true);
+    if (s) return s;
+    if (workspace_bytes < 0) return fail(BI8_ERR_SHAPE, "%s: workspace_bytes < 0", fn);
+    if (workspace && !aligned(workspace, 16))
+        return fail(BI8_ERR_ALIGN, "%s: the workspace must be 16-byte aligned", fn);
+    if (R == 0) return ok();
+    if (!expert_offsets) return fail(BI8_ERR_NULL, "%s: NULL expert_offsets", fn);
+    if (!aligned(expert_offsets, 4))
+        return fail(BI8_ERR_ALIGN, "%s: expert_offsets must be 4-byte aligned", fn);
+    return hip_status(fn, bi8::launch_moe_gemm_ws(xq, xs, expert_offsets, w, ws, y, R, N, K, E,
+                                                  static_cast<float *>(workspace), workspace_bytes,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
                            const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N,
                            int64_t K, int32_t E, int32_t block_n, int32_t block_k, void *stream) {

@@ -349,37 +349,55 @@ struct Tile {
     int64_t rows;  // valid activation rows in this tile
     const int8_t *w;
     const float *ws;
+    int32_t split = -1;   // grouped tail split: this unit's split of the tile (-1: the whole tile)
+    int32_t nsplit = 1;   // grouped tail split: splits of the tile
+    int64_t unit = 0;     // grouped tail split: the unit's partial-sum slot
 };
 
-template <int BN, int BM, bool MOE, int64_t GM = kGroupM>
-__device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
-    // MoE: the grid holds an upper bound of m-tiles (the segments' lengths are
-    // only known on the device); the tiles that exist are counted here and
-    // spread evenly over the XCDs, and the surplus workgroups exit.  (Mapped
-    // over the whole grid instead, the missing tiles -- all at the end of the
-    // order -- left the last XCD nearly idle: at R = 8192 over 8 experts the
-    // w13 grid gave six XCDs 560 tiles each and one XCD 56.)
-    int64_t tiles_m = p.tiles_m;
-    if constexpr (MOE) {
-        tiles_m = 0;
-        for (int32_t e = 0; e < p.E; ++e) {
-            int64_t a = p.offsets[e], b = p.offsets[e + 1];
-            a = a < 0 ? 0 : (a > p.M ? p.M : a);
-            b = b < a ? a : (b > p.M ? p.M : b);
-            tiles_m += (b - a + BM - 1) / BM;
-        }
+// Split tail of a grouped GEMM (one workgroup per CU): the tiles that exist,
+// T, fill F = 256 * floor(T / 256) whole rounds of the chip's CUs; the other
+// T - F run split over K into S parts each, so that their units fill one more
+// round.  S = min(256 / (T - F), KB, 16), trimmed so that no split is empty;
+// S = 1 when splitting would not shorten the last round.
+constexpr int64_t kTailRound = 256;
+struct TailPlan {
+    int64_t full;     // F
+    int64_t tail;     // T - F
+    int32_t splits;   // S
+    int64_t per;      // K blocks per split
+};
+__device__ __forceinline__ TailPlan tail_plan(int64_t total, int64_t KB) {
+    TailPlan t;
+    t.full = total / kTailRound * kTailRound;
+    t.tail = total - t.full;
+    int64_t s = t.tail > 0 ? kTailRound / t.tail : 1;
+    s = s < KB ? s : KB;
+    s = s < 16 ? s : 16;
+    s = s < 1 ? 1 : s;
+    t.per = (KB + s - 1) / s;
+    t.splits = (int32_t)((KB + t.per - 1) / t.per);
+    return t;
+}
+
+// The tiles that exist in a grouped GEMM with BM-row tiles: sum over the
+// expert segments (offsets clamped to [0, R]) of ceil(rows / BM).
+template <int BM>
+__device__ __forceinline__ int64_t moe_tiles_m(const GemmArgs &p) {
+    int64_t n = 0;
+    for (int32_t e = 0; e < p.E; ++e) {
+        int64_t a = p.offsets[e], b = p.offsets[e + 1];
+        a = a < 0 ? 0 : (a > p.M ? p.M : a);
+        b = b < a ? a : (b > p.M ? p.M : b);
+        n += (b - a + BM - 1) / BM;
     }
-    const int64_t total = tiles_m * p.tiles_n;
-    int64_t tid;
-    if constexpr (MOE) {
-        const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        const int64_t q = total >> 3, r = total & 7;
-        if (slot >= q + (xcd < r ? 1 : 0)) return false;
-        tid = xcd * q + (xcd < r ? xcd : r) + slot;
-    } else {
-        tid = xcd_remap(blockIdx.x, total);
-    }
-    // grouped order: GM m-tiles advance together along n
+    return n;
+}
+
+// Tile `tid` of the grouped order (GM m-tiles advance together along n) over
+// tiles_m m-tiles; for the grouped GEMM the m-tile is found by walking the
+// expert segments.
+template <int BN, int BM, bool MOE, int64_t GM>
+__device__ __forceinline__ bool tile_at(const GemmArgs &p, int64_t tid, int64_t tiles_m, Tile &t) {
     const int64_t group = tid / (GM * p.tiles_n);
     const int64_t first_m = group * GM;
     const int64_t gsize = tiles_m - first_m < GM ? tiles_m - first_m : GM;
@@ -412,6 +430,51 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
         }
         return false;
     }
+}
+
+template <int BN, int BM, bool MOE, int64_t GM = kGroupM, bool TAIL = false>
+__device__ __forceinline__ bool decode_tile(const GemmArgs &p, Tile &t) {
+    // MoE: the grid holds an upper bound of m-tiles (the segments' lengths are
+    // only known on the device); the tiles that exist are counted here and
+    // spread evenly over the XCDs, and the surplus workgroups exit.  (Mapped
+    // over the whole grid instead, the missing tiles -- all at the end of the
+    // order -- left the last XCD nearly idle: at R = 8192 over 8 experts the
+    // w13 grid gave six XCDs 560 tiles each and one XCD 56.)
+    // TAIL: workgroups [0, F) take the whole tiles of the full rounds (spread
+    // over the XCDs as above), workgroup F + u split unit u of the tail: tile
+    // F + u / S, split u % S.
+    static_assert(!TAIL || MOE, "split tails are the grouped GEMM's");
+    int64_t tiles_m = p.tiles_m;
+    if constexpr (MOE) tiles_m = moe_tiles_m<BM>(p);
+    const int64_t total = tiles_m * p.tiles_n;
+    int64_t tid;
+    if constexpr (MOE) {
+        int64_t balanced = total;
+        if constexpr (TAIL) {
+            const TailPlan tp = tail_plan(total, p.KB);
+            if (tp.splits > 1) {
+                balanced = tp.full;
+                if ((int64_t)blockIdx.x >= tp.full) {
+                    const int64_t u = (int64_t)blockIdx.x - tp.full;
+                    if (u >= tp.tail * tp.splits) return false;
+                    tid = tp.full + u / tp.splits;
+                    t.split = (int32_t)(u % tp.splits);
+                    t.nsplit = tp.splits;
+                    t.unit = u;
+                    balanced = -1;
+                }
+            }
+        }
+        if (balanced >= 0) {
+            const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+            const int64_t q = balanced >> 3, r = balanced & 7;
+            if (slot >= q + (xcd < r ? 1 : 0)) return false;
+            tid = xcd * q + (xcd < r ? xcd : r) + slot;
+        }
+    } else {
+        tid = xcd_remap(blockIdx.x, total);
+    }
+    return tile_at<BN, BM, MOE, GM>(p, tid, tiles_m, t);
 }
 
 // PING: the two wave groups (rows wm = 0 and wm = 1 of the wave grid; waves w
@@ -448,15 +511,28 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
     __shared__ float xsl[2][C::kBM * C::kSB];   // activation-scale batches, double-buffered
 
     Tile t;
-    if (!decode_tile<C::kBN, C::kBM, MOE>(p, t)) return;
+    // grouped with SPLIT: the full rounds' tiles whole, the tail's split over K
+    if (!decode_tile<C::kBN, C::kBM, MOE, kGroupM, MOE && SPLIT>(p, t)) return;
     if (t.rows <= 0) return;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t K = p.K;
-    // K blocks of this workgroup: [kb0, kb0 + KB); chunks at or past kend read zero
-    const int64_t kb0 = SPLIT ? (int64_t)blockIdx.y * p.kb_per_split : 0;
-    const int64_t KB = SPLIT ? (p.KB - kb0 < p.kb_per_split ? p.KB - kb0 : p.kb_per_split) : p.KB;
+    // K blocks of this workgroup: [kb0, kb0 + KB); chunks at or past kend read
+    // zero.  Dense split K: split blockIdx.y of kb_per_split blocks; grouped
+    // tail: split t.split of the tail plan's `per` blocks.
+    int64_t kb0 = 0, KB = p.KB;
+    if constexpr (SPLIT && !MOE) {
+        kb0 = (int64_t)blockIdx.y * p.kb_per_split;
+        KB = p.KB - kb0 < p.kb_per_split ? p.KB - kb0 : p.kb_per_split;
+    }
+    if constexpr (SPLIT && MOE) {
+        if (t.split >= 0) {
+            const int64_t per = (p.KB + t.nsplit - 1) / t.nsplit;
+            kb0 = (int64_t)t.split * per;
+            KB = p.KB - kb0 < per ? p.KB - kb0 : per;
+        }
+    }
     const int64_t kend = SPLIT ? ((kb0 + KB) * kBlock < K ? (kb0 + KB) * kBlock : K) : K;
 
     // Each range covers only this tile's rows (<= 2^31 bytes since K <= 2^23),
@@ -690,7 +766,27 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_tiled_kernel(GemmArgs p) {
 
     // Store.  32x32 result layout: lane -> token column (lane & 31); element i
     // -> weight row 8 * (i / 4) + 4 * (lane >> 5) + (i % 4).
-    if constexpr (SPLIT) {
+    if constexpr (SPLIT && MOE) {
+        if (t.split >= 0) {
+            // the unit's fp32 partial sums in its slot, [BM tile rows][BN tile
+            // columns], every row and column (moe_tail_reduce_kernel reads
+            // only the valid ones)
+            float *slot = p.partial + t.unit * (int64_t)(C::kBM * C::kBN);
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                float *prow = slot + (int64_t)(wm * C::kWaveM + b * 32 + rr) * C::kBN;
+#pragma unroll
+                for (int a = 0; a < SA; ++a)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const int c = wn * C::kWaveN + a * 32 + 8 * i4 + 4 * hi;
+                        *reinterpret_cast<f32x4 *>(prow + c) =
+                            f32x4{y[a][b][4 * i4], y[a][b][4 * i4 + 1], y[a][b][4 * i4 + 2], y[a][b][4 * i4 + 3]};
+                    }
+            }
+            return;
+        }
+    } else if constexpr (SPLIT) {
         // fp32 partial sums of this split, no bias, no rounding
         float *part = p.partial + (int64_t)blockIdx.y * p.M * p.N;
 #pragma unroll
@@ -1522,6 +1618,7 @@ template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3, false>(Ge
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4, false>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, true, 3, true>(GemmArgs);
 template __global__ void gemm_tiled_kernel<4, 2, 1, 1, false, false, 4, true>(GemmArgs);
+template __global__ void gemm_tiled_kernel<4, 2, 2, 2, true, true, 3, true>(GemmArgs);
 template __global__ void gemm_wide_kernel<false, false>(GemmArgs);
 template __global__ void gemm_perch_kernel<false>(GemmArgs);
 template __global__ void gemm_wide_kernel<true, false>(GemmArgs);
@@ -1583,6 +1680,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
         for (int32_t z = 1; z < splits; ++z) acc += partial[z * MN + i];
         if (bias) acc += bf16_bits_to_f32(bias[i % N]);
         y[i] = (uint16_t)(f32x2_to_bf16x2_bits(acc, 0.0f) & 0xFFFFu);
+    }
+}
+
+// Split tail of the grouped GEMM (BN x BM tiles): workgroup (i, z) adds, for
+// rows [z * BM / 8, (z + 1) * BM / 8) of tail tile F + i, the S partial sums
+// of its units in split order and stores bf16 -- the plan recomputed exactly
+// as the GEMM's decoder computed it.  Four outputs of one row per thread.
+template <int BN, int BM>
+__global__ __launch_bounds__(256) void moe_tail_reduce_kernel(GemmArgs p) {
+    const int64_t tiles_m = moe_tiles_m<BM>(p);
+    const TailPlan tp = tail_plan(tiles_m * p.tiles_n, p.KB);
+    if (tp.splits <= 1 || (int64_t)blockIdx.x >= tp.tail) return;
+    Tile t;
+    if (!tile_at<BN, BM, true, kGroupM>(p, tp.full + blockIdx.x, tiles_m, t)) return;
+    constexpr int kRows = BM / 8, kQuads = BN / 4;
+    const float *slots = p.partial + (int64_t)blockIdx.x * tp.splits * (BM * BN);
+    for (int idx = threadIdx.x; idx < kRows * kQuads; idx += 256) {
+        const int r = (int)blockIdx.y * kRows + idx / kQuads, c = (idx % kQuads) * 4;
+        const int64_t n = t.n0 + c;
+        if (r >= t.rows || n >= p.N) continue;
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(slots + r * BN + c);
+        for (int32_t z = 1; z < tp.splits; ++z)
+            acc += *reinterpret_cast<const f32x4 *>(slots + (int64_t)z * (BM * BN) + r * BN + c);
+        uint16_t *yrow = p.y + (t.m0 + r) * p.N;
+        if (p.wide_store && n + 4 <= p.N) {
+            *reinterpret_cast<uint2 *>(yrow + n) =
+                make_uint2(f32x2_to_bf16x2_bits(acc[0], acc[1]), f32x2_to_bf16x2_bits(acc[2], acc[3]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(acc[e], 0.0f) & 0xFFFFu);
+        }
     }
 }
 
@@ -1787,6 +1916,34 @@ hipError_t launch_moe_gemm(GemmPath path, const int8_t *xq, const float *xs, con
         default:
             return hipErrorInvalidValue;
     }
+}
+
+int64_t moe_gemm_workspace_bytes(int64_t R, int64_t N, int64_t K, int32_t E) {
+    if (select_moe_gemm_path(R, N, K, E) != GemmPath::kTile256x128) return 0;
+    return kTailRound * 256 * 128 * (int64_t)sizeof(float);   // one slot per unit of one round
+}
+
+hipError_t launch_moe_gemm_ws(const int8_t *xq, const float *xs, const int32_t *offsets, const int8_t *w,
+                              const float *ws, uint16_t *y, int64_t R, int64_t N, int64_t K, int32_t E,
+                              float *workspace, int64_t workspace_bytes, hipStream_t stream) {
+    const int64_t need = moe_gemm_workspace_bytes(R, N, K, E);
+    if (need == 0 || !workspace || workspace_bytes < need)
+        return launch_moe_gemm(GemmPath::kAuto, xq, xs, offsets, w, ws, y, R, N, K, E, stream);
+    GemmArgs p = make_args(xq, xs, w, ws, nullptr, y, R, N, K);
+    p.offsets = offsets;
+    p.E = E;
+    p.partial = workspace;
+    p.tiles_m = (R + 127) / 128 + E;   // >= sum over experts of ceil(rows_e / 128)
+    p.tiles_n = (N + 255) / 256;
+    // every tile of that bound, plus one round for the split units
+    const int64_t grid = p.tiles_m * p.tiles_n + kTailRound;
+    if (grid > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_tiled_kernel<4, 2, 2, 2, true, true, 3, true>), dim3((unsigned)grid), dim3(512), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((moe_tail_reduce_kernel<256, 128>), dim3((unsigned)kTailRound, 8), dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_moe_gemm_silu_quant(const int8_t *xq, const float *xs, const int32_t *offsets, const int8_t *w13,

@@ -64,6 +64,10 @@ hipError_t launch_linear(const uint16_t *x, int64_t ldx, const int8_t *w, const 
                          uint16_t *y, int64_t M, int64_t N, int64_t K, int32_t block_n, int32_t block_k,
                          int8_t *xq, float *xs, hipStream_t st);
 
+int64_t moe_gemm_workspace_bytes(int64_t R, int64_t N, int64_t K, int32_t E);
+hipError_t launch_moe_gemm_ws(const int8_t *xq, const float *xs, const int32_t *offsets, const int8_t *w,
+                              const float *ws, uint16_t *y, int64_t R, int64_t N, int64_t K, int32_t E,
+                              float *workspace, int64_t workspace_bytes, hipStream_t stream);
 hipError_t launch_moe_gemm_silu_quant(const int8_t *xq, const float *xs, const int32_t *offsets, const int8_t *w13,
                                       const float *ws13, int8_t *aq, float *as, int64_t R, int64_t I, int64_t K,
                                       int32_t E, hipStream_t stream);

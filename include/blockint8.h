@@ -188,6 +188,40 @@ int32_t blockint8_moe_gemm(const int8_t *xq, const float *xs, const int32_t *exp
                            int32_t block_n, int32_t block_k, void *stream);
 
 /*
+ * blockint8_moe_gemm with a caller workspace (section 6: the per-expert int8
+ * GEMMs of the fused-MoE runner).  When the tiles do not fill whole rounds of
+ * the chip's CUs, the tiles of the last, partial round run split over K into
+ * units that fill a round, and a second launch adds each such tile's fp32
+ * partial sums in split order and rounds to bf16 (deterministic; the other
+ * tiles are computed exactly as by blockint8_moe_gemm, and the split tiles
+ * differ from it only by the fp32 summation order).  The library still
+ * allocates nothing.
+ *
+ *   arguments as blockint8_moe_gemm, plus
+ *   workspace        device memory, 16-byte aligned, or NULL
+ *   workspace_bytes  its size; with less than
+ *                    blockint8_moe_gemm_workspace_size(R, N, K, E, 128, 128)
+ *                    (or NULL) the call is blockint8_moe_gemm
+ *
+ * Calls that overlap in time must not share a workspace.  Errors: as
+ * blockint8_moe_gemm; workspace_bytes < 0 -> BI8_ERR_SHAPE; a workspace not
+ * 16-byte aligned -> BI8_ERR_ALIGN.
+ */
+int32_t blockint8_moe_gemm_ws(const int8_t *xq, const float *xs, const int32_t *expert_offsets,
+                              const int8_t *w, const float *ws, uint16_t *y, int64_t R, int64_t N, int64_t K,
+                              int32_t E, int32_t block_n, int32_t block_k, void *workspace,
+                              int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes blockint8_moe_gemm_ws can use for a grouped problem: a
+ * fixed 32 MiB (one round of 256 x 128 fp32 partial tiles) when the grouped
+ * GEMM runs its 256 x 128 kernel, else 0 (and 0 for arguments the GEMM
+ * rejects).  A host rule: it reads no device memory.
+ */
+int64_t blockint8_moe_gemm_workspace_size(int64_t R, int64_t N, int64_t K, int32_t E, int32_t block_n,
+                                          int32_t block_k);
+
+/*
  * Dynamic-scale block-wise INT8 linear in one call: the activations are
  * quantised at run time (blockint8_quant_act) and fed to the block-scaled
  * GEMM (blockint8_gemm).  Section 4 of the page: the linear takes the input,

@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"blockint8_status_string", "blockint8_last_error",
                           "blockint8_quant_act", "blockint8_gemm", "blockint8_gemm_ws",
-                          "blockint8_gemm_workspace_size", "blockint8_moe_gemm",
+                          "blockint8_gemm_workspace_size", "blockint8_moe_gemm", "blockint8_moe_gemm_ws",
+                          "blockint8_moe_gemm_workspace_size",
                           "blockint8_linear", "blockint8_linear_noalloc", "blockint8_moe_route", "blockint8_quant_act_gather",
                           "blockint8_quant_weight", "blockint8_check_tp_partition",
                           "blockint8_silu_mul_quant", "blockint8_moe_gemm_silu_quant", "blockint8_moe_combine", "blockint8_gemm_select", "blockint8_moe_gemm_select",
@@ -149,6 +150,33 @@ def test_gemm_empty_is_noop(lib):
 def test_moe_rejects(lib, kw, status):
     assert moe(lib, **kw) == status
     assert lib.blockint8_last_error().decode().startswith("blockint8_moe_gemm")
+
+
+def moe_ws(lib, xq=P16, xs=P16, off=P16, w=P16, ws=P16, y=P16, R=4, N=256, K=256, E=2, bn=128, bk=128,
+           wsp=None, nbytes=0):
+    return lib.blockint8_moe_gemm_ws(xq, xs, off, w, ws, y, R, N, K, E, bn, bk, wsp, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(off=None), NULL), (dict(w=None), NULL), (dict(xq=None), NULL),
+    (dict(E=0), SHAPE), (dict(E=65537), SHAPE), (dict(R=-1), SHAPE), (dict(N=0), SHAPE),
+    (dict(nbytes=-1), SHAPE),
+    (dict(bn=64), BLOCK),
+    (dict(K=100), ALIGN), (dict(off=P16 + 2), ALIGN), (dict(wsp=P16 + 4, nbytes=1 << 25), ALIGN),
+])
+def test_moe_ws_rejects(lib, kw, status):
+    assert moe_ws(lib, **kw) == status
+    assert lib.blockint8_last_error().decode().startswith("blockint8_moe_gemm_ws")
+
+
+def test_moe_gemm_workspace_size_host_rule(lib):
+    mib32 = 256 * 128 * 256 * 4
+    assert bi8.moe_gemm_workspace_size(8192, 4096, 14336, 8) == mib32     # w2 of the MoE layer: 256 x 128
+    assert bi8.moe_gemm_workspace_size(700, 1024, 384, 3) == mib32
+    assert bi8.moe_gemm_workspace_size(8192, 28672, 4096, 8) == 0         # w13: the 256 x 256 kernel
+    for bad in [(0, 4096, 4096, 8), (8192, 0, 4096, 8), (8192, 4096, 100, 8), (8192, 4096, 4096, 0)]:
+        assert bi8.moe_gemm_workspace_size(*bad) == 0
+    assert lib.blockint8_moe_gemm_workspace_size(8192, 4096, 14336, 8, 64, 128) == 0
 
 
 def test_moe_empty_is_noop(lib):

@@ -197,6 +197,60 @@ def test_moe_gemm_silu_quant_is_the_unfused_pipeline(R, K, I, sizes):
     assert np.all(np.isfinite(z)) and np.all(z[:, :] >= 0)
 
 
+WS_CASES = [
+    # R, N, K, per-expert rows: every tile split (32 tiles, K in 3 blocks); 512
+    # full tiles and a split tail of 32; 256 tiles exactly (no tail, no split);
+    # a tail of 1 tile
+    (700, 1024, 384, [0, 300, 1, 399]),
+    (4100, 4096, 2048, [1025, 1000, 1075, 1000]),
+    (2048, 4096, 1024, [1024, 1024]),
+    (2049, 4096, 512, [1024, 1025]),
+]
+
+
+@pytest.mark.parametrize("R,N,K,sizes", WS_CASES)
+def test_moe_gemm_ws_split_tail(R, N, K, sizes):
+    """The grouped GEMM with a workspace (the last, partial round's tiles split
+    over K) against the one without (the tiles of the full rounds bit for bit,
+    the split tiles within the fp32 reassociation of their sums: one bf16 ulp)
+    and against the oracle on rows in every tile; with exactly representable
+    sums the two forms agree bit for bit everywhere."""
+    E = len(sizes)
+    rng = np.random.default_rng(R + N + K)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    xq = rng.integers(-127, 128, (R, K), dtype=np.int8)
+    xs = (rng.random((R, (K + 127) // 128)) * 1e-2 + 1e-3).astype(np.float32)
+    w = wl.weights(rng, E, N, K)
+    ws = wl.weight_scales(rng, E, *oracle.scale_shape(N, K))
+    nbytes = bi8.moe_gemm_workspace_size(R, N, K, E)
+    assert nbytes > 0, "the case must take the 256 x 128 kernel"
+    wsp = torch.empty(nbytes, dtype=torch.uint8, device=device())
+    d = [to_dev(a) for a in (xq, xs, off, w, ws)]
+    plain = bf16_bits(bi8.moe_gemm(*d))
+    y_buf = torch.full((R + 1, N), -1.0, dtype=torch.bfloat16, device=device())
+    split = bf16_bits(bi8.moe_gemm(*d, y=y_buf[:R], workspace=wsp))
+    assert np.all(bf16_bits(y_buf[R]) == bf16_bits(torch.tensor([-1.0], dtype=torch.bfloat16))[0])
+    assert np.all(np.isfinite(bits_to_f64(split)))
+    # reassociated fp32 sums: within a bf16 ulp of the row's largest output
+    # (relative to a single output near zero the difference may be larger)
+    g, r = bits_to_f64(split), bits_to_f64(plain)
+    row_max = np.abs(r).max(axis=1, keepdims=True)
+    assert np.all(np.abs(g - r) <= 2.0 ** -7 * row_max), "split tail outside the reassociation bound"
+    assert np.mean(split == plain) >= 0.99
+    split2 = bf16_bits(bi8.moe_gemm(*d, workspace=wsp))   # the workspace is reused: same result
+    assert np.array_equal(split, split2)
+    for e, rows in segment_tile_rows(off, 128, rng):
+        ref = oracle.gemm(xq[rows], xs[rows], w[e], ws[e])
+        assert_gemm_close(split[rows], ref, "expert %d" % e)
+    # exact sums: codes in [-3, 3], power-of-two scales
+    xq_e = rng.integers(-3, 4, (R, K), dtype=np.int8)
+    w_e = rng.integers(-3, 4, (E, N, K), dtype=np.int8)
+    xs_e = np.exp2(rng.integers(-4, 1, xs.shape)).astype(np.float32)
+    ws_e = np.exp2(rng.integers(-4, 1, ws.shape)).astype(np.float32)
+    d_e = [to_dev(a) for a in (xq_e, xs_e, off, w_e, ws_e)]
+    assert np.array_equal(bf16_bits(bi8.moe_gemm(*d_e, workspace=wsp)), bf16_bits(bi8.moe_gemm(*d_e)))
+
+
 def oracle_moe_layer(x, logits, w13, ws13, w2, ws2, k):
     T, H = x.shape
     E = logits.shape[1]
@@ -242,7 +296,7 @@ def test_moe_layer_end_to_end(T, H, I, E, k, variant):
 # layer end to end on 64 tokens covering every expert, against the oracle's
 # pipeline computed from the inputs alone.
 
-MOE_VARIANTS = [None, bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]
+MOE_VARIANTS = [None, "ws", bi8.GEMM_TILE_256X128, bi8.GEMM_TILE_256X256]   # "ws": default with a workspace
 
 
 @pytest.fixture(scope="module")
@@ -262,7 +316,10 @@ def moe_full():
     xq1, xs1 = bi8.quant_act_gather(d["x"], st)
     h = bi8.moe_gemm(xq1, xs1, off, d["w13"], d["ws13"])
     aq, as_, a = bi8.silu_mul_quant(h, return_a=True)
-    y2 = bi8.moe_gemm(aq, as_, off, d["w2"], d["ws2"])
+    # w2 as the layer runs it: with a workspace for a split last round
+    wsp_bytes = bi8.moe_gemm_workspace_size(aq.shape[0], H, I, E)
+    wsp = torch.empty(wsp_bytes, dtype=torch.uint8, device=device()) if wsp_bytes else None
+    y2 = bi8.moe_gemm(aq, as_, off, d["w2"], d["ws2"], workspace=wsp)
     out = bi8.moe_combine(y2, row_of, wts)
     out_layer = bi8.moe_layer(d["x"], d["logits"], d["w13"], d["ws13"], d["w2"], d["ws2"], k)
     aq_f, as_f = bi8.moe_gemm_silu_quant(xq1, xs1, off, d["w13"], d["ws13"])
@@ -270,7 +327,7 @@ def moe_full():
     host = dict(T=T, H=H, I=I, E=E, k=k, x=x, logits=logits, w13=w13, ws13=ws13, w2=w2, ws2=ws2,
                 ids=ids.cpu().numpy(), wts=wts.cpu().numpy(), st=st.cpu().numpy(), off=off.cpu().numpy(),
                 row_of=row_of.cpu().numpy(), out=bf16_bits(out), out_layer=bf16_bits(out_layer))
-    dev = dict(d, xq1=xq1, xs1=xs1, h=h, aq=aq, as_=as_, a=a, y2=y2, off=off, aq_f=aq_f, as_f=as_f)
+    dev = dict(d, xq1=xq1, xs1=xs1, h=h, aq=aq, as_=as_, a=a, y2=y2, off=off, aq_f=aq_f, as_f=as_f, wsp=wsp)
     yield host, dev
     del dev, d
     torch.cuda.empty_cache()
@@ -324,11 +381,15 @@ def test_moe_full_size_grouped_gemms(moe_full, variant):
     for e, rows in samples:
         q_ref, s_ref = oracle.quant_act(host["x"][host["st"][rows]])
         assert np.array_equal(xq1[rows], q_ref) and np.array_equal(xs1[rows], s_ref)
-    h = bf16_bits(bi8.moe_gemm(dev["xq1"], dev["xs1"], dev["off"], dev["w13"], dev["ws13"], variant=variant))
-    y2 = bf16_bits(bi8.moe_gemm(dev["aq"], dev["as_"], dev["off"], dev["w2"], dev["ws2"], variant=variant))
+    v = None if variant == "ws" else variant
+    h = bf16_bits(bi8.moe_gemm(dev["xq1"], dev["xs1"], dev["off"], dev["w13"], dev["ws13"], variant=v))
+    y2 = bf16_bits(bi8.moe_gemm(dev["aq"], dev["as_"], dev["off"], dev["w2"], dev["ws2"], variant=v,
+                                workspace=dev["wsp"] if variant == "ws" else None))
     assert np.all(np.isfinite(bits_to_f64(h))) and np.all(np.isfinite(bits_to_f64(y2)))
-    if variant is None:   # the layer's own intermediates are the default kernel's
-        assert np.array_equal(h, bf16_bits(dev["h"])) and np.array_equal(y2, bf16_bits(dev["y2"]))
+    if variant in (None, "ws"):   # the layer's own w13 is the default kernel's
+        assert np.array_equal(h, bf16_bits(dev["h"]))
+    if variant == "ws":           # and its w2 runs with the workspace
+        assert np.array_equal(y2, bf16_bits(dev["y2"]))
     refs = oracle_rows_pooled(
         lambda er: (oracle.gemm(xq1[er[1]], xs1[er[1]], host["w13"][er[0]], host["ws13"][er[0]]),
                     oracle.gemm(aq[er[1]], as_[er[1]], host["w2"][er[0]], host["ws2"][er[0]])), samples)
