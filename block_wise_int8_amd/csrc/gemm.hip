@@ -360,6 +360,7 @@ struct Tile {
 // round.  S = min(256 / (T - F), KB, 16), trimmed so that no split is empty;
 // S = 1 when splitting would not shorten the last round.
 constexpr int64_t kTailRound = 256;
+constexpr int64_t kTailMaxSplitsPlan = 16;   // at most this many splits per tail tile
 struct TailPlan {
     int64_t full;     // F
     int64_t tail;     // T - F
@@ -367,15 +368,18 @@ struct TailPlan {
     int64_t per;      // K blocks per split
 };
 __device__ __forceinline__ TailPlan tail_plan(int64_t total, int64_t KB) {
+    static_assert((kTailRound & (kTailRound - 1)) == 0, "power of two");
     TailPlan t;
-    t.full = total / kTailRound * kTailRound;
+    t.full = total & ~(kTailRound - 1);
     t.tail = total - t.full;
-    int64_t s = t.tail > 0 ? kTailRound / t.tail : 1;
-    s = s < KB ? s : KB;
-    s = s < 16 ? s : 16;
+    // (32-bit division: tail < 256 and KB <= 2^16, K being at most 2^23)
+    uint32_t s = t.tail > 0 ? (uint32_t)kTailRound / (uint32_t)t.tail : 1u;
+    s = s < KB ? s : (uint32_t)KB;
+    s = s < kTailMaxSplitsPlan ? s : (uint32_t)kTailMaxSplitsPlan;
     s = s < 1 ? 1 : s;
-    t.per = (KB + s - 1) / s;
-    t.splits = (int32_t)((KB + t.per - 1) / t.per);
+    const uint32_t kb = (uint32_t)KB;
+    t.per = (kb + s - 1) / s;
+    t.splits = (int32_t)((kb + (uint32_t)t.per - 1) / (uint32_t)t.per);
     return t;
 }
 
@@ -398,10 +402,12 @@ __device__ __forceinline__ int64_t moe_tiles_m(const GemmArgs &p) {
 // expert segments.
 template <int BN, int BM, bool MOE, int64_t GM>
 __device__ __forceinline__ bool tile_at(const GemmArgs &p, int64_t tid, int64_t tiles_m, Tile &t) {
-    const int64_t group = tid / (GM * p.tiles_n);
-    const int64_t first_m = group * GM;
-    const int64_t gsize = tiles_m - first_m < GM ? tiles_m - first_m : GM;
-    const int64_t in = tid - group * GM * p.tiles_n;
+    // (32-bit division: tid < 2^31 and GM * tiles_n < 2^31, both launch limits)
+    const uint32_t span = (uint32_t)(GM * p.tiles_n);
+    const uint32_t group = (uint32_t)tid / span;
+    const int64_t first_m = (int64_t)group * GM;
+    const uint32_t gsize = (uint32_t)(tiles_m - first_m < GM ? tiles_m - first_m : GM);
+    const uint32_t in = (uint32_t)tid - group * span;
     int64_t tm = first_m + in % gsize;
     const int64_t tn = in / gsize;
     t.n0 = tn * BN;
@@ -1683,34 +1689,60 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
-// Split tail of the grouped GEMM (BN x BM tiles): workgroup (i, z) adds, for
-// rows [z * BM / 8, (z + 1) * BM / 8) of tail tile F + i, the S partial sums
-// of its units in split order and stores bf16 -- the plan recomputed exactly
-// as the GEMM's decoder computed it.  Four outputs of one row per thread.
+// Split tail of the grouped GEMM (BN x BM tiles): for each row r of each tail
+// tile F + i, the S partial sums of its units added in split order and stored
+// as bf16 -- the plan recomputed exactly as the GEMM's decoder computed it.
+// A fixed grid (the tail's size is only known on the device); its waves take
+// the (tile, row) pairs in turn, lane l columns
+// [4l, 4l + 4) of every 256 columns, every split's load issued before the
+// first add.
+constexpr int kTailMaxSplits = 16;
+static_assert(kTailMaxSplitsPlan <= kTailMaxSplits, "the reduce holds every split");
+constexpr int kTailReduceWaves = 4;
+// 1024 workgroups: at the MoE w2 size (32 tail tiles x 128 rows) one
+// (tile, row) pair per wave, all loads in flight at once (256 workgroups:
+// 17 us, four pairs per wave one after another)
+#ifndef BI8_TAIL_REDUCE_BLOCKS
+#define BI8_TAIL_REDUCE_BLOCKS 1024
+#endif
+constexpr int kTailReduceBlocks = BI8_TAIL_REDUCE_BLOCKS;
 template <int BN, int BM>
-__global__ __launch_bounds__(256) void moe_tail_reduce_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kTailReduceWaves * 64) void moe_tail_reduce_kernel(GemmArgs p) {
     const int64_t tiles_m = moe_tiles_m<BM>(p);
     const TailPlan tp = tail_plan(tiles_m * p.tiles_n, p.KB);
-    if (tp.splits <= 1 || (int64_t)blockIdx.x >= tp.tail) return;
-    Tile t;
-    if (!tile_at<BN, BM, true, kGroupM>(p, tp.full + blockIdx.x, tiles_m, t)) return;
-    constexpr int kRows = BM / 8, kQuads = BN / 4;
-    const float *slots = p.partial + (int64_t)blockIdx.x * tp.splits * (BM * BN);
-    for (int idx = threadIdx.x; idx < kRows * kQuads; idx += 256) {
-        const int r = (int)blockIdx.y * kRows + idx / kQuads, c = (idx % kQuads) * 4;
-        const int64_t n = t.n0 + c;
-        if (r >= t.rows || n >= p.N) continue;
-        f32x4 acc = *reinterpret_cast<const f32x4 *>(slots + r * BN + c);
-        for (int32_t z = 1; z < tp.splits; ++z)
-            acc += *reinterpret_cast<const f32x4 *>(slots + (int64_t)z * (BM * BN) + r * BN + c);
+    if (tp.splits <= 1) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * kTailReduceWaves + (threadIdx.x >> 6);
+    const int64_t waves = (int64_t)gridDim.x * kTailReduceWaves;
+    for (int64_t pair = wave; pair < tp.tail * BM; pair += waves) {
+        const int64_t i = pair / BM;
+        const int r = (int)(pair - i * BM);
+        Tile t;
+        if (!tile_at<BN, BM, true, kGroupM>(p, tp.full + i, tiles_m, t)) continue;
+        if (r >= t.rows) continue;
+        const float *slots = p.partial + i * tp.splits * (BM * BN) + (int64_t)r * BN;
         uint16_t *yrow = p.y + (t.m0 + r) * p.N;
-        if (p.wide_store && n + 4 <= p.N) {
-            *reinterpret_cast<uint2 *>(yrow + n) =
-                make_uint2(f32x2_to_bf16x2_bits(acc[0], acc[1]), f32x2_to_bf16x2_bits(acc[2], acc[3]));
-        } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(acc[e], 0.0f) & 0xFFFFu);
+        for (int c0 = 0; c0 < BN; c0 += 256) {
+            const int c = c0 + 4 * lane;
+            const int64_t n = t.n0 + c;
+            if (n >= p.N) continue;
+            f32x4 part[kTailMaxSplits];
+#pragma unroll
+            for (int z = 0; z < kTailMaxSplits; ++z)
+                if (z < tp.splits) part[z] = *reinterpret_cast<const f32x4 *>(slots + (int64_t)z * (BM * BN) + c);
+            f32x4 acc = part[0];
+#pragma unroll
+            for (int z = 1; z < kTailMaxSplits; ++z)
+                if (z < tp.splits) acc += part[z];
+            if (p.wide_store && n + 4 <= p.N) {
+                *reinterpret_cast<uint2 *>(yrow + n) =
+                    make_uint2(f32x2_to_bf16x2_bits(acc[0], acc[1]), f32x2_to_bf16x2_bits(acc[2], acc[3]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < p.N) yrow[n + e] = (uint16_t)(f32x2_to_bf16x2_bits(acc[e], 0.0f) & 0xFFFFu);
+            }
         }
     }
 }
@@ -1942,7 +1974,8 @@ hipError_t launch_moe_gemm_ws(const int8_t *xq, const float *xs, const int32_t *
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((moe_tail_reduce_kernel<256, 128>), dim3((unsigned)kTailRound, 8), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((moe_tail_reduce_kernel<256, 128>), dim3((unsigned)kTailReduceBlocks),
+                       dim3(kTailReduceWaves * 64), 0, stream, p);
     return hipGetLastError();
 }
 
