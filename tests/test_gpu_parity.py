@@ -239,6 +239,36 @@ def test_gemm_integer_closed_form_bit_exact(M, N, K):
     assert np.array_equal(y, wl.to_bf16_bits(exact))
 
 
+@pytest.mark.parametrize("K", [16, 48, 144, 400, 1040, 1296, 2000, 4000, 4080])
+@pytest.mark.parametrize("offset", [0, 16, 48, 80])
+def test_gemm_rows_off_the_line_bit_exact(K, offset):
+    """Rows that do not start on a 128-byte line (K % 128 != 0, or operands at
+    a 16-byte offset from a line) through the small-grid kernel the library
+    picks and the forced 128 x 64 variant.  Unit scales and int8 activations:
+    y == bf16(int64 matmul) exactly, for every alignment of the rows, with a K
+    tail in the last block and several tiles."""
+    M, N = 200, 1000
+    rng = np.random.default_rng(K * 131 + offset)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    w = wl.weights(rng, N, K)
+    NB, KB = oracle.scale_shape(N, K)
+    exact = (xq.astype(np.int64) @ w.astype(np.int64).T)
+    assert np.abs(exact).max() < 2 ** 24   # every fp32 partial sum exact
+    dev = device()
+    xbuf = torch.zeros(offset + M * K + 256, dtype=torch.int8, device=dev)
+    wbuf = torch.zeros(offset + N * K + 256, dtype=torch.int8, device=dev)
+    xq_d = xbuf[offset:offset + M * K].view(M, K)
+    w_d = wbuf[offset:offset + N * K].view(N, K)
+    xq_d.copy_(torch.from_numpy(xq))
+    w_d.copy_(torch.from_numpy(w))
+    xs = torch.ones((M, KB), dtype=torch.float32, device=dev)
+    ws = torch.ones((NB, KB), dtype=torch.float32, device=dev)
+    for v in (None, bi8.GEMM_TILE_128X64):
+        y = bf16_bits(bi8.gemm(xq_d, xs, w_d, ws, variant=v))
+        assert np.array_equal(y, wl.to_bf16_bits(exact.astype(np.float32))), "K=%d offset=%d variant %s" % (
+            K, offset, v)
+
+
 @pytest.mark.parametrize("M,N,K", [(7, 300, 528), (150, 600, 528)])
 def test_gemm_power_of_two_bit_exact(M, N, K):
     """Power-of-two scales, |xq| <= 31: every partial sum exact in fp32.
