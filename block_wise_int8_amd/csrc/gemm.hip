@@ -338,6 +338,10 @@ constexpr int64_t kSplitKTarget = BI8_SPLITK_TARGET;
 constexpr int64_t kSplitKMaxOutputs = 640 * 1024;
 constexpr int kSplitKStages = BI8_SPLITK_STAGES;
 constexpr int64_t kGroupMWide = 4;
+// Grouped GEMM: at most this many m-tiles of one expert advance together
+// along n (the workload's experts hold 4-5 tiles of 256 rows and 8-9 of 128:
+// each is one group).  Measured at the MoE size: 8 and 32 within 1 %.
+constexpr int64_t kGroupMMoe = 16;
 #ifndef BI8_TILED_SPREAD_FILLS
 #define BI8_TILED_SPREAD_FILLS 1
 #endif
@@ -397,27 +401,29 @@ __device__ __forceinline__ int64_t moe_tiles_m(const GemmArgs &p) {
     return n;
 }
 
-// Tile `tid` of the grouped order (GM m-tiles advance together along n) over
-// tiles_m m-tiles; for the grouped GEMM the m-tile is found by walking the
-// expert segments.
+// Tile `tid` of the grouped order over tiles_m m-tiles: groups of GM m-tiles
+// advance together along n, so the tiles that share a weight tile run side by
+// side.  For the grouped GEMM the groups follow the expert segments: expert e's
+// m-tiles (found by walking the segments) in groups of at most kGroupMMoe, so
+// that no group mixes two experts' weights (groups across segment boundaries
+// read both experts' weight tiles, and most of the weights twice).
 template <int BN, int BM, bool MOE, int64_t GM>
 __device__ __forceinline__ bool tile_at(const GemmArgs &p, int64_t tid, int64_t tiles_m, Tile &t) {
     // (32-bit division: tid < 2^31 and GM * tiles_n < 2^31, both launch limits)
-    const uint32_t span = (uint32_t)(GM * p.tiles_n);
-    const uint32_t group = (uint32_t)tid / span;
-    const int64_t first_m = (int64_t)group * GM;
-    const uint32_t gsize = (uint32_t)(tiles_m - first_m < GM ? tiles_m - first_m : GM);
-    const uint32_t in = (uint32_t)tid - group * span;
-    int64_t tm = first_m + in % gsize;
-    const int64_t tn = in / gsize;
-    t.n0 = tn * BN;
     if constexpr (!MOE) {
-        t.m0 = tm * BM;
+        const uint32_t span = (uint32_t)(GM * p.tiles_n);
+        const uint32_t group = (uint32_t)tid / span;
+        const int64_t first_m = (int64_t)group * GM;
+        const uint32_t gsize = (uint32_t)(tiles_m - first_m < GM ? tiles_m - first_m : GM);
+        const uint32_t in = (uint32_t)tid - group * span;
+        t.n0 = (int64_t)(in / gsize) * BN;
+        t.m0 = (first_m + in % gsize) * BM;
         t.rows = p.M - t.m0 < BM ? p.M - t.m0 : BM;
         t.w = p.w;
         t.ws = p.ws;
         return true;
     } else {
+        int64_t rem = tid;
         for (int32_t e = 0; e < p.E; ++e) {
             // clamp to [0, R] so that offsets breaking the precondition can
             // never address rows outside xq / y
@@ -425,14 +431,21 @@ __device__ __forceinline__ bool tile_at(const GemmArgs &p, int64_t tid, int64_t 
             a = a < 0 ? 0 : (a > p.M ? p.M : a);
             b = b < a ? a : (b > p.M ? p.M : b);
             const int64_t cnt = (b - a + BM - 1) / BM;
-            if (tm < cnt) {
-                t.m0 = a + tm * BM;
+            const int64_t espan = cnt * p.tiles_n;
+            if (rem < espan) {
+                const uint32_t span = (uint32_t)(kGroupMMoe * p.tiles_n);
+                const uint32_t group = (uint32_t)rem / span;
+                const int64_t first_m = (int64_t)group * kGroupMMoe;
+                const uint32_t gsize = (uint32_t)(cnt - first_m < kGroupMMoe ? cnt - first_m : kGroupMMoe);
+                const uint32_t in = (uint32_t)rem - group * span;
+                t.n0 = (int64_t)(in / gsize) * BN;
+                t.m0 = a + (first_m + in % gsize) * BM;
                 t.rows = b - t.m0 < BM ? b - t.m0 : BM;
                 t.w = p.w + (int64_t)e * p.N * p.K;
                 t.ws = p.ws + (int64_t)e * p.NB * p.KB;
                 return true;
             }
-            tm -= cnt;
+            rem -= espan;
         }
         return false;
     }
