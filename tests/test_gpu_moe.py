@@ -205,6 +205,8 @@ WS_CASES = [
     (4100, 4096, 2048, [1025, 1000, 1075, 1000]),
     (2048, 4096, 1024, [1024, 1024]),
     (2049, 4096, 512, [1024, 1025]),
+    # one expert of 33 m-tiles (three tile groups), tail tiles split
+    (4300, 2048, 512, [4200, 100]),
 ]
 
 

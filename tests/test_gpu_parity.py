@@ -431,6 +431,9 @@ def moe_case(seed, counts, N, K):
     ([7, 0, 130, 1, 0, 257], 300, 400),
     ([0, 0, 128], 128, 128),
     ([300, 5, 33, 128, 129], 512, 1024),
+    # experts longer than one tile group (16 m-tiles): 33 and 17 tiles of 128
+    # rows, 17 and 9 of 256, so a group boundary falls inside an expert
+    ([4200, 0, 2100, 3], 512, 256),
 ])
 @pytest.mark.parametrize("variant", MOE_VARIANTS)
 def test_moe_small_vs_oracle(counts, N, K, variant):
